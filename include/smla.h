@@ -1,0 +1,155 @@
+/*
+ * smla.h -- head-batched sparse Multi-head Latent Attention decode for AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (per query row r = (b, s) and head h):
+ *   L      = the valid entries of indices[b, s, :] (logical token positions);
+ *   K_p    = the latent row of token p: c_kv (d_v values) followed by k_rope
+ *            (d_qk - d_v values); V_p = its c_kv part;
+ *   score  = softmax_scale * Q[r, h, :] . K_p           for p in L;
+ *   out    = sum_p softmax(score)_p * V_p,  lse = ln sum_p exp(score_p).
+ * Each selected latent row is read from the cache once and shared by all
+ * heads; the top-k list is cut into num_splits parts computed by separate
+ * workgroups, whose partial (out, lse) pairs are merged by a log-sum-exp
+ * combine kernel.
+ *
+ * Sources (page title, then section):
+ *   - "The MMA Sparse-MLA Decode Kernel: A Deep Dive into AI Inference
+ *     Optimization on Blackwell GPUs", Agent Reasoning: "Kernel Structure
+ *     Analysis" (query parts, latent rows as keys and values), "Cache Layout
+ *     Understanding" (paged per-token latent cache, fp8 part with per-group
+ *     scales, bf16 rope part), "Design Decisions" 1 (one program serves a
+ *     group of heads with one KV load), 3 (split-K over top-k with a combine
+ *     kernel), 6 (fp32 accumulation, bf16 only at the store), "Edge Case
+ *     Handling" (tokens past the valid length are excluded), "Validation
+ *     Strategy" (results are the output and the log-sum-exp).
+ *   - "The Moment of Truth: Analyzing a Custom MMA Kernel's Performance on
+ *     Blackwell GPUs": "The Occupancy Problem: A Deeper Dive" (a grid of
+ *     batch x head-groups starves the GPU at small batch) and "The Split-K
+ *     Solution: Reasoning About the Fix" (split count fixed per batch
+ *     bucket so the launch is graph-safe; deterministic scratch size).
+ *
+ * Conventions:
+ *   - Every buffer is owned by the caller.  The library allocates no device
+ *     memory and keeps no mutable global state (the CU count of each device
+ *     is cached).  Pointers are device pointers unless marked "host".
+ *   - smla_decode_run and smla_combine are asynchronous on `stream` (a
+ *     hipStream_t; NULL = the null stream): no host synchronisation, no
+ *     allocation, a launch geometry that depends only on the plan.
+ *   - Errors are returned as smla_status_t; nothing throws or aborts.  Host
+ *     checks cover null pointers, sizes and the workspace size.  Bad index
+ *     values on the device are not errors: they are masked (see
+ *     smla_decode_run).
+ *   - All tensors are dense row-major with the shapes given.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_INVALID_ARG = 1,          /* null pointer, negative or inconsistent size */
+    SMLA_ERR_UNSUPPORTED = 2,          /* a shape this library does not implement */
+    SMLA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < plan->workspace_bytes */
+    SMLA_ERR_LAUNCH = 4,               /* the HIP runtime rejected a launch */
+    SMLA_ERR_DEVICE = 5                /* the HIP runtime failed a device query */
+} smla_status_t;
+
+typedef enum {
+    /* bf16 latent rows: d_qk bf16 values (c_kv then k_rope), 2*d_qk bytes. */
+    SMLA_KV_BF16 = 0,
+    /* fp8 latent rows: d_v OCP e4m3fn bytes (c_kv), then (d_qk-d_v) bf16
+     * k_rope values, then d_v/128 little-endian fp32 scales; c_kv element d
+     * is e4m3(byte d) * scale[d/128].  656 bytes for d_qk=576, d_v=512. */
+    SMLA_KV_FP8_E4M3_SCALE128 = 1
+} smla_kv_format_t;
+
+/* Problem description (host).  Supported: num_heads = 64, d_qk = 576,
+ * d_v = 512, block_size = 64; any batch >= 0, q_len >= 1, topk >= 0. */
+typedef struct {
+    int32_t batch;               /* B: sequences */
+    int32_t q_len;               /* query tokens per sequence, each with its own top-k list */
+    int32_t num_heads;           /* H */
+    int32_t d_qk;                /* latent row width used by QK^T (c_kv + rope) */
+    int32_t d_v;                 /* value width (the c_kv part) */
+    int32_t topk;                /* index entries per query row */
+    int32_t block_size;          /* tokens per cache block */
+    int32_t max_blocks_per_seq;  /* columns of the block table */
+    int32_t kv_format;           /* smla_kv_format_t */
+    int32_t num_cus;             /* compute units to fill; 0 = query the current device */
+    int32_t force_splits;        /* 0 = choose automatically; > 0 = use this split count (clamped to the tile count) */
+    int32_t reserved;            /* must be 0 */
+} smla_problem_t;
+
+/* Plan: a pure function of the problem (identical problems give identical
+ * plans), so a captured launch sequence stays valid for its batch bucket. */
+typedef struct {
+    smla_problem_t prob;
+    int32_t rows;                /* batch * q_len */
+    int32_t num_splits;          /* S: parts of the top-k list */
+    int32_t tokens_per_split;    /* tokens per part (a multiple of tile_tokens, except through clamping) */
+    int32_t tile_tokens;         /* tokens per gathered tile */
+    int32_t heads_per_group;     /* heads served by one workgroup */
+    int32_t num_workgroups;      /* workgroups of the partial-attention kernel */
+    uint64_t workspace_bytes;    /* bytes of device workspace smla_decode_run needs (0 if S = 1) */
+} smla_plan_t;
+
+/*
+ * Fill *plan_out for *prob.  Host only; touches the device only when
+ * prob->num_cus == 0 (to read the current device's CU count).
+ * Returns SMLA_ERR_INVALID_ARG for null pointers or negative sizes,
+ * SMLA_ERR_UNSUPPORTED for shapes outside the supported set,
+ * SMLA_ERR_DEVICE if the CU count cannot be read.
+ */
+smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out);
+
+/*
+ * Sparse MLA decode.  Shapes (R = batch * q_len, H = num_heads):
+ *   q            bf16  [batch, q_len, H, d_qk]
+ *   kv_cache     bytes [num_kv_blocks, block_size, row_bytes(kv_format)]
+ *   block_table  int32 [batch, max_blocks_per_seq]: physical block of each
+ *                logical block of a sequence
+ *   indices      int32 [batch, q_len, topk]: logical token positions; -1 pads
+ *   seq_lens     int32 [batch] or NULL
+ *   out          bf16  [batch, q_len, H, d_v]   (fp32 accumulation, rounded to nearest even)
+ *   lse          fp32  [batch, q_len, H]        natural-log log-sum-exp of the scaled scores
+ *   workspace    >= plan->workspace_bytes bytes, 256-byte aligned (may be NULL if 0)
+ * An index entry p of sequence b is masked (takes no part) when p < 0,
+ * p >= block_size * max_blocks_per_seq, p >= seq_lens[b] (if given), or its
+ * block-table entry lies outside [0, num_kv_blocks).  A row with no valid
+ * entry gets out = 0 and lse = -inf.  Repeated entries count once each.
+ * Returns SMLA_OK after enqueueing the kernels on `stream`.
+ */
+smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void *kv_cache,
+                              int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,
+                              const int32_t *seq_lens, float softmax_scale, void *out, float *lse,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Log-sum-exp merge of partial attention results over disjoint parts of a
+ * list ("The Moment of Truth: Analyzing a Custom MMA Kernel's Performance
+ * on Blackwell GPUs", "The Split-K Solution: Reasoning About the Fix").
+ *   part_out  fp32 [num_splits, rows, num_heads, d_v]: per-part normalised outputs
+ *   part_lse  fp32 [num_splits, rows, num_heads]: per-part lse, -inf for an empty part
+ *   out       bf16 [rows, num_heads, d_v];  lse fp32 [rows, num_heads]
+ * out = sum_i exp(lse_i - lse) * part_out_i with lse = ln sum_i exp(lse_i);
+ * parts with lse_i = -inf carry no weight; if every part is empty,
+ * out = 0 and lse = -inf.  Supported: d_v a multiple of 4, num_splits >= 1.
+ */
+smla_status_t smla_combine(const float *part_out, const float *part_lse, int32_t num_splits, int32_t rows,
+                           int32_t num_heads, int32_t d_v, void *out, float *lse, void *stream);
+
+/* Static text for a status code (host). */
+const char *smla_status_string(smla_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

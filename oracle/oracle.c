@@ -1,0 +1,336 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for head-batched sparse MLA decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or constant with the GPU library; the two meet only at the byte
+ * layout of the inputs, which both sides implement separately.
+ *
+ * What is computed (the plain definition, no blocking, no online softmax):
+ *   For every query row r = (b, s) and head h, over the list L of valid
+ *   selected token positions of that row,
+ *       score_j = scale * sum_{d < d_qk} Q[r,h,d] * K_{L_j}[d]
+ *       m       = max_j score_j,   Z = sum_j exp(score_j - m)
+ *       lse     = m + ln Z                         (natural log)
+ *       out[d]  = sum_j exp(score_j - m) * V_{L_j}[d] / Z,   d < d_v
+ *   K is the whole latent row of a token (the c_kv part followed by the rope
+ *   part) and V is the c_kv part of the same row.
+ *   Sources:
+ *   - "The MMA Sparse-MLA Decode Kernel: A Deep Dive into AI Inference
+ *     Optimization on Blackwell GPUs", Agent Reasoning, "Kernel Structure
+ *     Analysis": the query carries a non-positional and a rotary part, and
+ *     the cached latent rows serve as both keys and values for all heads.
+ *   - same page, "Cache Layout Understanding": a paged per-token latent
+ *     cache, partly fp8 with per-group scales, partly bf16 rope.
+ *   - same page, "Edge Case Handling": tokens past the valid length take no
+ *     part in the softmax.
+ *   - same page, "Validation Strategy": the kernel's results are the output
+ *     and the log-sum-exp per head.
+ *   - "The Moment of Truth: Analyzing a Custom MMA Kernel's Performance on
+ *     Blackwell GPUs", "The Split-K Solution: Reasoning About the Fix": the
+ *     top-k list may be cut into chunks whose partial results are merged by
+ *     a combine step (oracle_lse_combine below).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - an index is a logical position in its sequence; the block table maps
+ *     position p to physical block table[b][p / block_size], slot
+ *     p % block_size;
+ *   - an index is invalid (masked) if it is negative, >= seq_lens[b] (when
+ *     seq_lens is given), >= block_size * max_blocks_per_seq, or if its
+ *     block-table entry is outside [0, num_kv_blocks);
+ *   - the list is a multiset: a repeated index counts once per occurrence;
+ *   - a row with no valid index yields out = 0 and lse = -inf.
+ *
+ * Byte layout of one token row (row_bytes per token, rows of a block are
+ * contiguous, blocks are contiguous):
+ *   kv_format 0 (bf16):  d_qk bf16 values, 2*d_qk bytes.
+ *   kv_format 1 (fp8):   d_v  OCP e4m3fn bytes (the c_kv part), then
+ *                        (d_qk-d_v) bf16 rope values, then d_v/128 fp32
+ *                        scales; c_kv element d is e4m3(byte d) * scale[d/128].
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+/* bf16: 1 sign bit, 8 exponent bits (bias 127), 7 mantissa bits. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int m = h & 0x7f;
+    double v;
+    if (e == 0xff)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -133);            /* m/128 * 2^(1-127) */
+    else
+        v = ldexp(1.0 + m / 128.0, e - 127);
+    return sign ? -v : v;
+}
+
+/* OCP fp8 e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN. */
+double oracle_e4m3fn_to_f64(uint8_t x)
+{
+    int sign = (x >> 7) & 1;
+    int e = (x >> 3) & 0xf;
+    int m = x & 0x7;
+    double v;
+    if (e == 0xf && m == 0x7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);              /* m/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* IEEE binary32 stored little-endian. */
+static double f32_le_to_f64(const uint8_t *p)
+{
+    uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    int sign = (u >> 31) & 1;
+    int e = (u >> 23) & 0xff;
+    uint32_t m = u & 0x7fffff;
+    double v;
+    if (e == 0xff)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -149);
+    else
+        v = ldexp(1.0 + m / 8388608.0, e - 127);
+    return sign ? -v : v;
+}
+
+static uint16_t load_u16_le(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+void oracle_bf16_array_to_f64(int64_t n, const uint16_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f64(in[i]);
+}
+
+void oracle_e4m3fn_array_to_f64(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3fn_to_f64(in[i]);
+}
+
+int64_t oracle_row_bytes(int32_t kv_format, int32_t d_qk, int32_t d_v)
+{
+    if (kv_format == 0) return 2 * (int64_t)d_qk;
+    if (kv_format == 1) return (int64_t)d_v + 2 * (int64_t)(d_qk - d_v) + 4 * (int64_t)(d_v / 128);
+    return -1;
+}
+
+/* Decode one token row into K[0..d_qk). */
+static void decode_token_row(int32_t kv_format, int32_t d_qk, int32_t d_v, const uint8_t *row, double *k)
+{
+    if (kv_format == 0) {
+        for (int d = 0; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(row + 2 * d));
+    } else {
+        const uint8_t *rope = row + d_v;
+        const uint8_t *scales = row + d_v + 2 * (d_qk - d_v);
+        for (int d = 0; d < d_v; ++d) k[d] = oracle_e4m3fn_to_f64(row[d]) * f32_le_to_f64(scales + 4 * (d / 128));
+        for (int d = d_v; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(rope + 2 * (d - d_v)));
+    }
+}
+
+typedef struct {
+    int32_t batch, q_len, num_heads, d_qk, d_v, topk, block_size, max_blocks_per_seq, kv_format;
+    int64_t num_kv_blocks;
+    const uint16_t *q;
+    const uint8_t *kv_cache;
+    const int32_t *block_table;
+    const int32_t *indices;
+    const int32_t *seq_lens;
+    double scale;
+    double *out;
+    double *lse;
+    int64_t next_row;
+    int error;
+    pthread_mutex_t lock;
+} decode_job;
+
+/* Physical row of logical position p in sequence b, or -1 if p is masked. */
+static int64_t physical_row(const decode_job *J, int b, int32_t p)
+{
+    int64_t cap = (int64_t)J->block_size * J->max_blocks_per_seq;
+    if (J->seq_lens && (int64_t)J->seq_lens[b] < cap) cap = J->seq_lens[b];
+    if (p < 0 || (int64_t)p >= cap) return -1;
+    int32_t blk = J->block_table[(int64_t)b * J->max_blocks_per_seq + p / J->block_size];
+    if (blk < 0 || (int64_t)blk >= J->num_kv_blocks) return -1;
+    return (int64_t)blk * J->block_size + p % J->block_size;
+}
+
+static void decode_one_row(decode_job *J, int64_t r, double *kbuf, double *score, double *qrow)
+{
+    const int H = J->num_heads, DQK = J->d_qk, DV = J->d_v;
+    const int b = (int)(r / J->q_len);
+    const int64_t row_bytes = oracle_row_bytes(J->kv_format, DQK, DV);
+    const int32_t *idx = J->indices + r * J->topk;
+
+    /* Valid list L, decoded once and shared by all heads. */
+    int n = 0;
+    for (int j = 0; j < J->topk; ++j) {
+        int64_t pr = physical_row(J, b, idx[j]);
+        if (pr < 0) continue;
+        decode_token_row(J->kv_format, DQK, DV, J->kv_cache + pr * row_bytes, kbuf + (int64_t)n * DQK);
+        ++n;
+    }
+
+    for (int h = 0; h < H; ++h) {
+        double *o = J->out + (r * H + h) * DV;
+        const uint16_t *qh = J->q + (r * H + h) * DQK;
+        if (n == 0) {
+            for (int d = 0; d < DV; ++d) o[d] = 0.0;
+            J->lse[r * H + h] = -INFINITY;
+            continue;
+        }
+        for (int d = 0; d < DQK; ++d) qrow[d] = oracle_bf16_to_f64(qh[d]);
+        double m = -INFINITY;
+        for (int j = 0; j < n; ++j) {
+            const double *k = kbuf + (int64_t)j * DQK;
+            double acc = 0.0;
+            for (int d = 0; d < DQK; ++d) acc += qrow[d] * k[d];
+            score[j] = J->scale * acc;
+            if (score[j] > m) m = score[j];
+        }
+        double z = 0.0;
+        for (int j = 0; j < n; ++j) {
+            score[j] = exp(score[j] - m);      /* now the unnormalised weight */
+            z += score[j];
+        }
+        for (int d = 0; d < DV; ++d) o[d] = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const double *v = kbuf + (int64_t)j * DQK;  /* V = first d_v of K */
+            for (int d = 0; d < DV; ++d) o[d] += score[j] * v[d];
+        }
+        for (int d = 0; d < DV; ++d) o[d] /= z;
+        J->lse[r * H + h] = m + log(z);
+    }
+}
+
+static void *decode_worker(void *arg)
+{
+    decode_job *J = (decode_job *)arg;
+    double *kbuf = (double *)malloc(sizeof(double) * (size_t)(J->topk > 0 ? J->topk : 1) * J->d_qk);
+    double *score = (double *)malloc(sizeof(double) * (size_t)(J->topk > 0 ? J->topk : 1));
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)J->d_qk);
+    if (!kbuf || !score || !qrow) {
+        pthread_mutex_lock(&J->lock);
+        J->error = ORACLE_NO_MEMORY;
+        pthread_mutex_unlock(&J->lock);
+        free(kbuf); free(score); free(qrow);
+        return NULL;
+    }
+    const int64_t rows = (int64_t)J->batch * J->q_len;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t r = J->next_row++;
+        pthread_mutex_unlock(&J->lock);
+        if (r >= rows) break;
+        decode_one_row(J, r, kbuf, score, qrow);
+    }
+    free(kbuf); free(score); free(qrow);
+    return NULL;
+}
+
+/*
+ * q:           bf16 [batch, q_len, num_heads, d_qk]
+ * kv_cache:    bytes [num_kv_blocks, block_size, row_bytes]
+ * block_table: int32 [batch, max_blocks_per_seq]
+ * indices:     int32 [batch, q_len, topk]
+ * seq_lens:    int32 [batch] or NULL
+ * out:         f64 [batch, q_len, num_heads, d_v]
+ * lse:         f64 [batch, q_len, num_heads]
+ * Rows are split over num_threads POSIX threads (<= 0 means 1); the
+ * arithmetic of a row does not depend on the thread count.
+ */
+int oracle_sparse_mla_decode(int32_t batch, int32_t q_len, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                             int32_t topk, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_kv_blocks, int32_t kv_format,
+                             const uint16_t *q, const uint8_t *kv_cache, const int32_t *block_table,
+                             const int32_t *indices, const int32_t *seq_lens, double scale,
+                             double *out, double *lse, int32_t num_threads)
+{
+    if (batch < 0 || q_len <= 0 || num_heads <= 0 || d_v <= 0 || d_qk < d_v || topk < 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_kv_blocks < 0)
+        return ORACLE_BAD_ARG;
+    if (kv_format != 0 && kv_format != 1) return ORACLE_BAD_ARG;
+    if (kv_format == 1 && d_v % 128 != 0) return ORACLE_BAD_ARG;
+    if ((int64_t)batch * q_len == 0) return ORACLE_OK;
+    if (!q || !kv_cache || !block_table || !indices || !out || !lse) return ORACLE_BAD_ARG;
+
+    decode_job J;
+    memset(&J, 0, sizeof(J));
+    J.batch = batch; J.q_len = q_len; J.num_heads = num_heads; J.d_qk = d_qk; J.d_v = d_v;
+    J.topk = topk; J.block_size = block_size; J.max_blocks_per_seq = max_blocks_per_seq;
+    J.kv_format = kv_format; J.num_kv_blocks = num_kv_blocks;
+    J.q = q; J.kv_cache = kv_cache; J.block_table = block_table; J.indices = indices;
+    J.seq_lens = seq_lens; J.scale = scale; J.out = out; J.lse = lse;
+    J.next_row = 0; J.error = ORACLE_OK;
+    pthread_mutex_init(&J.lock, NULL);
+
+    int nt = num_threads <= 0 ? 1 : num_threads;
+    if (nt > 256) nt = 256;
+    if (nt == 1) {
+        decode_worker(&J);
+    } else {
+        pthread_t th[256];
+        int started = 0;
+        for (int i = 0; i < nt; ++i)
+            if (pthread_create(&th[i], NULL, decode_worker, &J) == 0) ++started;
+        if (started == 0) decode_worker(&J);
+        for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    }
+    pthread_mutex_destroy(&J.lock);
+    return J.error;
+}
+
+/*
+ * Merge of partial attention results over disjoint parts of one list
+ * ("The Split-K Solution: Reasoning About the Fix": partial results over
+ * chunks of the top-k dimension are reduced by a combine step; the pages'
+ * kernel-design page also names the log-sum-exp as the quantity carried).
+ * For each of n (row, head) pairs, given S partial outputs o_i (normalised
+ * over part i) and their log-sum-exps lse_i:
+ *     M = max_i lse_i;  if M = -inf the result is (0, -inf);
+ *     lse = M + ln sum_i exp(lse_i - M);  out = sum_i exp(lse_i - lse) * o_i.
+ * part_out: f64 [S, n, d_v]; part_lse: f64 [S, n]; out: f64 [n, d_v]; lse: f64 [n].
+ */
+int oracle_lse_combine(int32_t num_splits, int64_t n, int32_t d_v, const double *part_out,
+                       const double *part_lse, double *out, double *lse)
+{
+    if (num_splits <= 0 || n < 0 || d_v <= 0) return ORACLE_BAD_ARG;
+    if (n == 0) return ORACLE_OK;
+    if (!part_out || !part_lse || !out || !lse) return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        double M = -INFINITY;
+        for (int s = 0; s < num_splits; ++s) {
+            double v = part_lse[(int64_t)s * n + i];
+            if (v > M) M = v;
+        }
+        double *o = out + i * d_v;
+        for (int d = 0; d < d_v; ++d) o[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double z = 0.0;
+        for (int s = 0; s < num_splits; ++s) z += exp(part_lse[(int64_t)s * n + i] - M);
+        double total = M + log(z);
+        for (int s = 0; s < num_splits; ++s) {
+            if (part_lse[(int64_t)s * n + i] == -INFINITY) continue;   /* an empty part has zero weight */
+            double w = exp(part_lse[(int64_t)s * n + i] - total);
+            const double *po = part_out + ((int64_t)s * n + i) * d_v;
+            for (int d = 0; d < d_v; ++d) o[d] += w * po[d];
+        }
+        lse[i] = total;
+    }
+    return ORACLE_OK;
+}

@@ -1,0 +1,339 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError if
+the oracle disagrees with:
+
+* textbook dense attention written with numpy matrix products and an
+  independent numpy/torch decoding of the cache bytes (when the top-k list
+  covers every token of the sequence);
+* invariances of the definition: order of the index list, split of the list
+  into parts merged by the log-sum-exp combine, placement of blocks in the
+  paged cache, masking by -1 / out-of-range entries;
+* closed forms: a single selected token, a zero query, identical rows,
+  repeated indices, and the combine's own special cases;
+* library conversions (torch) of every bf16 and e4m3fn bit pattern.
+
+The same battery is run against deliberately broken copies of the oracle
+source to show that plausible mistakes are caught.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from sparse_mla_decode_smla_amd import inputs as I
+
+# ----------------------------------------------------------------- helpers
+
+
+def np_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 via the fp32 upper-half definition."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def np_e4m3(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def token_rows(inp: I.Inputs, b: int, positions: np.ndarray) -> np.ndarray:
+    """Decoded latent rows K [n, d_qk] (float64) of logical positions of sequence b."""
+    w = inp.workload
+    bs, rb = w.block_size, w.row_bytes
+    flat = inp.kv_cache.reshape(-1, rb)
+    positions = np.asarray(positions, dtype=np.int64)
+    phys = inp.block_table[b, positions // bs].astype(np.int64) * bs + positions % bs
+    raw = flat[phys]
+    if w.kv_format == I.KV_BF16:
+        return np_bf16(np.ascontiguousarray(raw).view(np.uint16).reshape(len(positions), w.d_qk))
+    dr = w.d_qk - w.d_v
+    c = np_e4m3(raw[:, : w.d_v])
+    scales = np.ascontiguousarray(raw[:, w.d_v + 2 * dr:]).view(np.float32).astype(np.float64)
+    c = c * np.repeat(scales, 128, axis=1)
+    rope = np_bf16(np.ascontiguousarray(raw[:, w.d_v: w.d_v + 2 * dr]).view(np.uint16))
+    return np.concatenate([c, rope], axis=1)
+
+
+def dense_attention(inp: I.Inputs, b: int, s: int, positions: np.ndarray):
+    """Textbook softmax(Q K^T * scale) V over the given positions (numpy matmuls)."""
+    w = inp.workload
+    K = token_rows(inp, b, positions)
+    Q = np_bf16(inp.q[b, s])                         # [H, d_qk]
+    S = (Q @ K.T) * inp.softmax_scale                # [H, n]
+    m = S.max(axis=1, keepdims=True)
+    P = np.exp(S - m)
+    Z = P.sum(axis=1, keepdims=True)
+    out = (P @ K[:, : w.d_v]) / Z
+    lse = (m + np.log(Z))[:, 0]
+    return out, lse
+
+
+def assert_close(got, ref, rtol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    scale = max(1.0, float(np.abs(ref).max())) if ref.size else 1.0
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3g}"
+
+
+def run_rows(orc, inp: I.Inputs, indices: np.ndarray, with_seq_lens=True):
+    return orc.decode_inputs(inp, indices=indices, with_seq_lens=with_seq_lens)
+
+
+# ----------------------------------------------------------------- decode tables
+
+
+def pin_bf16_table(orc):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "bf16 NaN patterns differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "bf16 decode differs from torch"
+
+
+def pin_e4m3_table(orc):
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    ref = np_e4m3(codes)
+    got = orc.e4m3fn_to_f64(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2, "torch should report exactly two e4m3fn NaN codes"
+    assert (np.isnan(got) == nan).all(), "e4m3fn NaN codes differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "e4m3fn decode differs from torch"
+
+
+# ----------------------------------------------------------------- dense brute force
+
+
+def _dense_pin(orc, inp: I.Inputs):
+    out, lse = orc.decode_inputs(inp)
+    w = inp.workload
+    for b in range(w.batch):
+        n_b = int(inp.seq_lens[b])
+        for s in range(w.q_len):
+            row = inp.indices[b, s]
+            assert sorted(row[row >= 0].tolist()) == list(range(n_b)), "test setup: list must cover the sequence"
+            ref_o, ref_l = dense_attention(inp, b, s, np.arange(n_b))
+            assert_close(out[b, s], ref_o, 1e-12, f"dense out b{b} s{s}")
+            assert_close(lse[b, s], ref_l, 1e-12, f"dense lse b{b} s{s}")
+
+
+def pin_dense_bf16(orc):
+    _dense_pin(orc, I.small_inputs(batch=2, q_len=2, topk=256, seq_len=256, kv_format=I.KV_BF16, seed=1))
+
+
+def pin_dense_fp8(orc):
+    _dense_pin(orc, I.small_inputs(batch=2, q_len=2, topk=256, seq_len=256, kv_format=I.KV_FP8, seed=2))
+
+
+def pin_dense_ragged_padded(orc):
+    # lengths 60..200 with top-k 200: every list covers its sequence, short ones padded with -1
+    _dense_pin(orc, I.small_inputs(batch=4, q_len=1, topk=200, seq_len_range=(60, 200), kv_format=I.KV_BF16,
+                                   seed=3))
+
+
+# ----------------------------------------------------------------- invariances
+
+
+def pin_permutation(orc):
+    inp = I.small_inputs(batch=2, q_len=2, topk=160, seq_len=512, kv_format=I.KV_FP8, seed=4)
+    out, lse = orc.decode_inputs(inp)
+    rng = np.random.default_rng(40)
+    perm_idx = inp.indices.copy()
+    for b in range(perm_idx.shape[0]):
+        for s in range(perm_idx.shape[1]):
+            perm_idx[b, s] = rng.permutation(perm_idx[b, s])
+    out2, lse2 = orc.decode_inputs(inp, indices=perm_idx)
+    assert_close(out2, out, 1e-12, "permuted out")
+    assert_close(lse2, lse, 1e-12, "permuted lse")
+
+
+def pin_split_combine(orc):
+    inp = I.small_inputs(batch=2, q_len=1, topk=150, seq_len=512, kv_format=I.KV_BF16, seed=5)
+    out, lse = orc.decode_inputs(inp)
+    rng = np.random.default_rng(50)
+    topk = inp.indices.shape[2]
+    for S in (2, 3, 5):
+        cuts = np.sort(rng.integers(0, topk + 1, size=S - 1))
+        if S == 5:
+            cuts[1] = cuts[0]      # one empty part
+        bounds = [0, *cuts.tolist(), topk]
+        parts_o, parts_l = [], []
+        for a, c in zip(bounds[:-1], bounds[1:]):
+            o, l = orc.decode_inputs(inp, indices=np.ascontiguousarray(inp.indices[:, :, a:c]))
+            parts_o.append(o)
+            parts_l.append(l)
+        co, cl = orc.lse_combine(np.stack(parts_o), np.stack(parts_l))
+        assert_close(co, out, 1e-12, f"combine of {S} parts, out")
+        assert_close(cl, lse, 1e-12, f"combine of {S} parts, lse")
+
+
+def pin_paging(orc):
+    inp = I.small_inputs(batch=3, q_len=1, topk=100, seq_len=320, kv_format=I.KV_FP8, seed=6)
+    out, lse = orc.decode_inputs(inp)
+    w = inp.workload
+    bs = w.block_size
+    nblk = (inp.seq_lens.astype(np.int64) + bs - 1) // bs
+    cache2 = np.zeros_like(inp.kv_cache)
+    bt2 = np.zeros_like(inp.block_table)
+    off = 0
+    for b in range(w.batch):
+        for j in range(nblk[b]):
+            cache2[off + j] = inp.kv_cache[inp.block_table[b, j]]
+            bt2[b, j] = off + j
+        off += int(nblk[b])
+    out2, lse2 = orc.sparse_mla_decode(inp.q, cache2, bt2, inp.indices, inp.seq_lens, inp.softmax_scale,
+                                       d_v=w.d_v, kv_format=w.kv_format, block_size=bs)
+    assert np.array_equal(out2, out) and np.array_equal(lse2, lse), "block placement changed the result"
+
+
+def pin_masking(orc):
+    inp = I.small_inputs(batch=2, q_len=2, topk=120, seq_len=300, kv_format=I.KV_BF16, seed=7)
+    w = inp.workload
+    rng = np.random.default_rng(70)
+    cap = w.block_size * inp.block_table.shape[1]
+    idx = inp.indices.copy()
+    seq_lens = inp.seq_lens.copy()
+    seq_lens[1] = 250                                  # positions 250..299 of sequence 1 become invalid
+    bt = inp.block_table.copy()
+    bt[0, 2] = -5                                      # positions 128..191 of sequence 0: bad block id
+    bt[1, 0] = inp.kv_cache.shape[0] + 3               # positions 0..63 of sequence 1: block id past the cache
+    for b in range(w.batch):
+        for s in range(w.q_len):
+            pos = rng.choice(idx.shape[2], size=30, replace=False)
+            kinds = rng.integers(0, 3, size=30)
+            idx[b, s, pos[kinds == 0]] = -1
+            idx[b, s, pos[kinds == 1]] = -7
+            idx[b, s, pos[kinds == 2]] = cap + 11
+    out, lse = orc.sparse_mla_decode(inp.q, inp.kv_cache, bt, idx, seq_lens, inp.softmax_scale,
+                                     d_v=w.d_v, kv_format=w.kv_format, block_size=w.block_size)
+    for b in range(w.batch):
+        for s in range(w.q_len):
+            row = idx[b, s]
+            keep = (row >= 0) & (row < min(cap, seq_lens[b]))
+            blk_ok = np.zeros_like(keep)
+            blk_ok[keep] = [(0 <= bt[b, p // w.block_size] < inp.kv_cache.shape[0]) for p in row[keep]]
+            keep &= blk_ok
+            sub = np.ascontiguousarray(row[keep][None, None, :])
+            o1, l1 = orc.sparse_mla_decode(inp.q[b:b + 1, s:s + 1], inp.kv_cache, bt[b:b + 1], sub,
+                                           seq_lens[b:b + 1], inp.softmax_scale, d_v=w.d_v,
+                                           kv_format=w.kv_format, block_size=w.block_size)
+            assert np.array_equal(out[b, s], o1[0, 0]) and np.array_equal(lse[b, s], l1[0, 0]), \
+                f"masked entries changed row ({b}, {s})"
+
+
+def pin_seq_lens_mask(orc):
+    inp = I.small_inputs(batch=2, q_len=1, topk=256, seq_len=256, kv_format=I.KV_FP8, seed=8)
+    seq_lens = np.array([256, 100], dtype=np.int32)
+    w = inp.workload
+    out, lse = orc.sparse_mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.indices, seq_lens,
+                                     inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format,
+                                     block_size=w.block_size)
+    ref_o, ref_l = dense_attention(inp, 1, 0, np.arange(100))
+    assert_close(out[1, 0], ref_o, 1e-12, "seq_lens-limited out")
+    assert_close(lse[1, 0], ref_l, 1e-12, "seq_lens-limited lse")
+
+
+def pin_empty_row(orc):
+    inp = I.small_inputs(batch=2, q_len=1, topk=64, seq_len=128, kv_format=I.KV_BF16, seed=9)
+    idx = inp.indices.copy()
+    idx[1] = -1
+    out, lse = orc.decode_inputs(inp, indices=idx)
+    assert np.all(out[1] == 0.0), "an empty row must give out = 0"
+    assert np.all(lse[1] == -np.inf), "an empty row must give lse = -inf"
+    assert np.isfinite(lse[0]).all()
+
+
+# ----------------------------------------------------------------- closed forms
+
+
+def pin_single_token(orc):
+    inp = I.small_inputs(batch=2, q_len=2, topk=48, seq_len=256, kv_format=I.KV_FP8, seed=10)
+    idx = np.full_like(inp.indices, -1)
+    rng = np.random.default_rng(100)
+    for b in range(2):
+        for s in range(2):
+            idx[b, s, rng.integers(0, 48)] = rng.integers(0, 256)
+    out, lse = orc.decode_inputs(inp, indices=idx)
+    w = inp.workload
+    for b in range(2):
+        for s in range(2):
+            p = int(idx[b, s][idx[b, s] >= 0][0])
+            K = token_rows(inp, b, np.array([p]))[0]
+            assert np.array_equal(out[b, s], np.broadcast_to(K[: w.d_v], out[b, s].shape)), \
+                "one token: out must equal its V row exactly"
+            ref_l = (np_bf16(inp.q[b, s]) @ K) * inp.softmax_scale
+            assert_close(lse[b, s], ref_l, 1e-12, "one token: lse = scaled score")
+
+
+def pin_zero_query(orc):
+    inp = I.small_inputs(batch=1, q_len=1, topk=77, seq_len=256, kv_format=I.KV_BF16, seed=11)
+    q0 = np.zeros_like(inp.q)
+    w = inp.workload
+    out, lse = orc.sparse_mla_decode(q0, inp.kv_cache, inp.block_table, inp.indices, inp.seq_lens,
+                                     inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format,
+                                     block_size=w.block_size)
+    K = token_rows(inp, 0, inp.indices[0, 0])
+    ref = np.broadcast_to(K[:, : w.d_v].mean(axis=0), out[0, 0].shape)
+    assert_close(out[0, 0], ref, 1e-13, "zero query: out = mean of V rows")
+    assert_close(lse[0, 0], np.full(w.num_heads, math.log(77)), 1e-14, "zero query: lse = ln n")
+
+
+def pin_identical_rows(orc):
+    inp = I.small_inputs(batch=1, q_len=1, topk=90, seq_len=256, kv_format=I.KV_FP8, seed=12)
+    kv = inp.kv_cache.copy()
+    kv[:] = kv[0, 0]                                    # every token row identical
+    w = inp.workload
+    out, lse = orc.sparse_mla_decode(inp.q, kv, inp.block_table, inp.indices, inp.seq_lens,
+                                     inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format,
+                                     block_size=w.block_size)
+    inp2 = I.Inputs(**{**inp.__dict__, "kv_cache": kv})
+    K = token_rows(inp2, 0, np.array([0]))[0]
+    assert_close(out[0, 0], np.broadcast_to(K[: w.d_v], out[0, 0].shape), 1e-13, "identical rows: out = V")
+    s = (np_bf16(inp.q[0, 0]) @ K) * inp.softmax_scale
+    assert_close(lse[0, 0], s + math.log(90), 1e-12, "identical rows: lse = s + ln n")
+
+
+def pin_duplicates(orc):
+    inp = I.small_inputs(batch=1, q_len=1, topk=3, seq_len=128, kv_format=I.KV_BF16, seed=13)
+    idx = np.array([[[17, 17, 90]]], dtype=np.int32)
+    out, lse = orc.decode_inputs(inp, indices=idx)
+    w = inp.workload
+    K = token_rows(inp, 0, np.array([17, 90]))
+    sc = (np_bf16(inp.q[0, 0]) @ K.T) * inp.softmax_scale      # [H, 2]
+    wts = np.exp(sc) * np.array([2.0, 1.0])
+    ref = (wts @ K[:, : w.d_v]) / wts.sum(axis=1, keepdims=True)
+    assert_close(out[0, 0], ref, 1e-12, "repeated index counts twice: out")
+    assert_close(lse[0, 0], np.log(wts.sum(axis=1)), 1e-12, "repeated index counts twice: lse")
+
+
+def pin_combine_closed_forms(orc):
+    rng = np.random.default_rng(14)
+    o = rng.standard_normal((1, 3, 5, 8))
+    l = rng.standard_normal((1, 3, 5))
+    co, cl = orc.lse_combine(o, l)
+    assert np.array_equal(co, o[0]) and np.array_equal(cl, l[0]), "one part: combine is the identity"
+    o2 = rng.standard_normal((2, 4, 8))
+    l2 = np.stack([np.full(4, 0.7), np.full(4, 0.7)])
+    co, cl = orc.lse_combine(o2, l2)
+    assert_close(co, (o2[0] + o2[1]) / 2, 1e-15, "equal lse: average")
+    assert_close(cl, np.full(4, 0.7 + math.log(2)), 1e-15, "equal lse: lse + ln 2")
+    l3 = np.array([[-np.inf, 1.5], [2.0, -np.inf]])
+    o3 = rng.standard_normal((2, 2, 8))
+    o3[0, 0] = np.nan                                  # an empty part's values carry no weight
+    co, cl = orc.lse_combine(o3, l3)
+    assert np.array_equal(co[0], o3[1, 0]) and cl[0] == 2.0
+    assert np.array_equal(co[1], o3[0, 1]) and cl[1] == 1.5
+    co, cl = orc.lse_combine(np.ones((3, 2, 8)), np.full((3, 2), -np.inf))
+    assert np.all(co == 0.0) and np.all(cl == -np.inf), "all parts empty: (0, -inf)"
+
+
+ALL_PINS = [
+    pin_bf16_table, pin_e4m3_table, pin_dense_bf16, pin_dense_fp8, pin_dense_ragged_padded,
+    pin_permutation, pin_split_combine, pin_paging, pin_masking, pin_seq_lens_mask, pin_empty_row,
+    pin_single_token, pin_zero_query, pin_identical_rows, pin_duplicates, pin_combine_closed_forms,
+]

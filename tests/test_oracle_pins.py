@@ -1,0 +1,9 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin, oracle_lib):
+    pin(oracle_lib)
