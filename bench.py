@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark: head-batched sparse MLA decode on one MI355X.
+
+One step = one ``smla_decode_run`` call (partial-attention kernel, plus the
+log-sum-exp combine kernel when the plan splits the top-k list) over one
+batch of synthetic, seeded inputs already resident in HBM.  The default
+workload is batch 1, 64 heads, top-k 2048 over a 32768-token paged bf16
+latent cache (1152-byte rows).
+
+Timing: W eager warm-up steps, then K steps captured in one HIP graph and
+replayed once between torch.cuda.synchronize() calls, timed with events on
+the stream the kernels run on.  The graph removes host launch gaps so the
+time is the GPU's.  Cold cache: consecutive steps cycle over R copies of the
+cache (R * gathered bytes >= 1 GiB, four times the 256 MB Infinity Cache),
+so a step's rows are not still cached from the previous visit.
+
+Output: one JSON line.  ``value`` = gathered-KV GB/s of the whole call
+(gathered bytes = valid selected tokens * row bytes).  ``roofline`` is for
+the partial-attention kernel alone: its time is the graph time per call minus
+the combine kernel's time (timed the same way on the same partials).
+``cpu_baseline`` times the fp64 oracle on the host for a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode µs/call + gathered-KV HBM GB/s (% peak), B=1..128, H=64"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "b1_topk2048_n32768_paged_bf16"
+ROTATION_BYTES = 1 << 30
+MAX_COPY_BYTES = 48 << 30
+KERNEL_SOURCES = ["sparse_mla_decode_smla_amd/csrc/smla_decode.hip",
+                  "sparse_mla_decode_smla_amd/csrc/smla_combine.hip",
+                  "sparse_mla_decode_smla_amd/csrc/smla_internal.h",
+                  "sparse_mla_decode_smla_amd/csrc/smla_plan.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
+    import oracle
+    w = inp.workload
+    threads = max(1, min(w.rows, os.cpu_count() or 1, 16))
+    # bounded sample: whole sequences (all their query rows), enough of them for the threads
+    nseq = max(1, min(w.batch, threads))
+    sel = list(range(nseq))
+    rows = nseq * w.q_len
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.default().sparse_mla_decode(inp.q[sel], inp.kv_cache, inp.block_table[sel], inp.indices[sel],
+                                           inp.seq_lens[sel], inp.softmax_scale, d_v=w.d_v,
+                                           kv_format=w.kv_format, block_size=w.block_size,
+                                           threads=min(threads, rows))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    sample_bytes = inp.valid_count(inp.indices[sel]) * w.row_bytes * reps
+    return {"value": round(sample_bytes / el / 1e9, 6), "unit": "GB/s", "cores": min(threads, rows),
+            "kind": "oracle",
+            "sample": f"{reps} x {nseq} sequence(s) ({rows} query rows, all 64 heads) of the workload, "
+                      f"{el:.1f} s fp64 on the host"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-splits", type=int, default=0, help="override the planned split count (sweeps)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_decode_smla_amd import binding as B
+    from sparse_mla_decode_smla_amd import inputs as I
+
+    w = I.WORKLOADS_BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}")
+    inp = I.make_inputs(w, seed=0)
+    gathered = inp.valid_count() * w.row_bytes
+    q, kv, bt, idx, sl = B.to_device(inp, device=dev)
+    plan = B.decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format,
+                         force_splits=args.force_splits)
+    out = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
+    ws = B.alloc_workspace(plan, dev)
+
+    cache_bytes = kv.numel()
+    R = max(2, math.ceil(ROTATION_BYTES / max(gathered, 1)))
+    R = min(R, max(2, MAX_COPY_BYTES // max(cache_bytes, 1)), 1024)
+    log(f"[bench] plan splits={plan.num_splits} tokens/split={plan.tokens_per_split} "
+        f"workgroups={plan.num_workgroups}; cache copies for rotation: {R}")
+    copies = [kv] + [kv.clone() for _ in range(R - 1)]
+    scale = inp.softmax_scale
+
+    def step(i):
+        B.decode_run(plan, q, copies[i % R], bt, idx, sl, scale, out, lse, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+
+    # eager per-call time (includes host launch gaps), for reference only
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_eager = min(args.steps, 100)
+    e0.record()
+    for i in range(n_eager):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / n_eager
+
+    K = args.steps
+    stream = torch.cuda.Stream(device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+        log("[bench] graph replay result differs from the eager result")
+        return 1
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        graph.replay()
+        s1.record(stream)
+    torch.cuda.synchronize()
+    call_us = s0.elapsed_time(s1) * 1e3 / K
+
+    # combine kernel alone, on the same partials, same way
+    combine_us = 0.0
+    if plan.num_splits > 1:
+        S, rows = plan.num_splits, plan.rows
+        pairs = rows * w.num_heads
+        part_out = ws[: S * pairs * w.d_v * 4].view(torch.float32).view(S, rows, w.num_heads, w.d_v)
+        part_lse = ws[S * pairs * w.d_v * 4: S * pairs * (w.d_v + 1) * 4].view(torch.float32).view(
+            S, rows, w.num_heads)
+        out2 = torch.empty_like(out).view(rows, w.num_heads, w.d_v)
+        lse2 = torch.empty_like(lse).view(rows, w.num_heads)
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g2, stream=stream):
+                for _ in range(K):
+                    B.combine(part_out, part_lse, out2, lse2)
+        g2.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            g2.replay()
+            c1.record(stream)
+        torch.cuda.synchronize()
+        combine_us = c0.elapsed_time(c1) * 1e3 / K
+    partial_us = max(call_us - combine_us, 1e-3)
+
+    gbs = gathered / (call_us * 1e-6) / 1e9
+    kernel_gbs = gathered / (partial_us * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(inp, gathered, args.cpu_seconds)
+
+    fmt_name = "bf16" if w.kv_format == I.KV_BF16 else "fp8e4m3+bf16"
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(call_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_format == I.KV_BF16 else "fp8e4m3/bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "heads": w.num_heads,
+                   "topk": w.topk, "seq_len": w.seq_len if w.seq_len else list(w.seq_len_range),
+                   "kv_format": fmt_name, "row_bytes": w.row_bytes, "gathered_bytes": gathered,
+                   "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
+                   "workgroups": plan.num_workgroups, "cache": f"cold: {R} rotating cache copies"},
+        "us_per_call": round(call_us, 3),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_call_eager": round(eager_us, 3),
+        "kernels_us": {"partial": round(partial_us, 3), "combine": round(combine_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

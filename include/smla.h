@@ -116,6 +116,7 @@ smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out
  *   block_table  int32 [batch, max_blocks_per_seq]: physical block of each
  *                logical block of a sequence
  *   indices      int32 [batch, q_len, topk]: logical token positions; -1 pads
+ *                (may be NULL when topk == 0)
  *   seq_lens     int32 [batch] or NULL
  *   out          bf16  [batch, q_len, H, d_v]   (fp32 accumulation, rounded to nearest even)
  *   lse          fp32  [batch, q_len, H]        natural-log log-sum-exp of the scaled scores

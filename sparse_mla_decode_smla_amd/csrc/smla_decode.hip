@@ -1,0 +1,498 @@
+// Partial-attention kernel of head-batched sparse MLA decode, and the
+// smla_decode_run entry point.
+//
+// One workgroup handles one query row (b, s), all 64 heads, and one part of
+// that row's top-k list.  Every selected latent row is gathered from the
+// paged cache into LDS once and read from there by all four waves (wave w
+// owns heads [16w, 16w + 16)): the head batching of "The MMA Sparse-MLA
+// Decode Kernel: A Deep Dive into AI Inference Optimization on Blackwell
+// GPUs" (Agent Reasoning, "Design Decisions" 1 and "Memory Budgeting"), here
+// with all 64 heads in one workgroup since a gfx950 CU has 160 KB of LDS.
+// Cutting the list into parts is the split-K of "The Moment of Truth:
+// Analyzing a Custom MMA Kernel's Performance on Blackwell GPUs" ("The
+// Split-K Solution: Reasoning About the Fix"); each part writes a normalised
+// partial output and its log-sum-exp, merged by the combine kernel.
+//
+// Per tile of 32 tokens:
+//   gather  : 16-byte LDS-DMA loads (global_load_lds_dwordx4) of whole rows,
+//             pipelined over a ring of LDS stages; masked tokens load zeros;
+//   QK^T    : S^T[token, head] = K . Q^T with v_mfma_f32_16x16x32_bf16,
+//             Q held in registers, K read from LDS (fp8 rows are widened to
+//             bf16 in registers; the per-128 fp32 scale multiplies the
+//             per-group partial scores);
+//   softmax : online, base 2, running max and sum per head in registers,
+//             masked tokens get -inf ("Edge Case Handling": invalid tokens
+//             never enter the softmax);
+//   PV      : O^T[dim, head] += V^T . P^T with the same MFMA; V^T comes from
+//             the same LDS tile through transpose reads (ds_read_b64_tr_b16,
+//             ds_read_b64_tr_b8); fp32 accumulation, bf16 only at the store
+//             ("Design Decisions" 6).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace smla {
+
+smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
+                             int d_v, void* out, float* lse, hipStream_t stream);
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Source of the 16-byte loads of masked tokens: their LDS slots become zeros,
+// so a masked token contributes 0 * 0 to the PV product.
+__device__ __attribute__((aligned(16))) const unsigned char kZeroChunk[16] = {0};
+
+struct PartialArgs {
+    const uint16_t* q;
+    const uint8_t* kv;
+    const int32_t* block_table;
+    const int32_t* indices;
+    const int32_t* seq_lens;
+    uint16_t* out;
+    float* lse;
+    float* part_out;
+    float* part_lse;
+    int64_t num_kv_blocks;
+    int32_t rows, q_len, topk, max_blocks, tokens_per_split, num_splits;
+    float scale_log2;
+};
+
+// 16-byte LDS-DMA load: lane l's 16 bytes from `src` land at LDS byte
+// lds_base + 16*l.  Issued from inline assembly so the compiler does not
+// serialise the stage ring with conservative waits; the kernel waits on
+// vmcnt itself.  M0 is written only here (the kernel has no other M0 use).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// XOR swizzle of the eight 16-byte chunks of a band, by token.  bf16: the
+// 16-byte QK reads of 8 consecutive tokens and the 8-byte transpose reads of
+// 4 consecutive tokens both hit distinct banks.  fp8: the same for the QK
+// reads of tokens {0-3, 8-11}(+4) and the transpose reads of 8 consecutive
+// tokens.
+template <int FMT>
+__device__ __forceinline__ int swz(int t) {
+    if (FMT == 0) return ((t & 3) << 1) | ((t >> 2) & 1);
+    return (t & 3) | ((((t >> 2) ^ (t >> 3)) & 1) << 2);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_u8* p) {
+    return *(const __attribute__((address_space(3))) T*)p;
+}
+
+// Eight e4m3fn codes (two dwords) -> eight bf16 (exact).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(unsigned lo, unsigned hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void partial_kernel(PartialArgs a) {
+    constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : kStageBytesFp8;
+    constexpr int NST = FMT == 0 ? kStagesBf16 : kStagesFp8;
+    constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : kRowBytesFp8;
+    constexpr int NBANDS = FMT == 0 ? kBandsBf16 : kBandsFp8;
+    constexpr int LPT = NBANDS + (FMT == 0 ? 0 : 1);  // DMA instructions per wave per tile
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_generic[];
+    lds_u8* lds = (lds_u8*)smem_generic;
+    const unsigned lds0 = (unsigned)(uintptr_t)lds;
+    lds_u8* rowtab = lds + NST * STAGE;  // int32 per token of this part: physical row or -1
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;    // 16-lane group
+    const int i16 = lane & 15;  // lane within the group
+
+    const int r = blockIdx.x / a.num_splits;
+    const int sp = blockIdx.x - r * a.num_splits;
+    const int b = r / a.q_len;
+    const int k0 = sp * a.tokens_per_split;
+    const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
+    const int ntiles = (nk + kTile - 1) / kTile;
+
+    // ---- logical positions -> physical rows (masked entries -> -1)
+    {
+        int64_t cap = (int64_t)kBlock * a.max_blocks;
+        if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
+        const int32_t* idx = a.indices + (int64_t)r * a.topk + k0;
+        const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+        for (int i = tid; i < ntiles * kTile; i += kThreads) {
+            int row = -1;
+            if (i < nk) {
+                const int pos = idx[i];
+                if (pos >= 0 && (int64_t)pos < cap) {
+                    const int blk = bt[pos / kBlock];
+                    if (blk >= 0 && (int64_t)blk < a.num_kv_blocks) row = blk * kBlock + (pos % kBlock);
+                }
+            }
+            *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
+        }
+    }
+
+    // ---- Q of this wave's 16 heads, as the B operand of S^T = K . Q^T.
+    // Lane (i16, g) holds head 16*wave + i16, 8 dims per k-step.  For fp8
+    // rows the c_kv dims of k-steps 2p and 2p+1 inside a 128-group are the
+    // two halves of one 16-byte run, so one LDS read feeds two k-steps.
+    bf16x8 qreg[18];
+    {
+        const uint16_t* qh = a.q + ((int64_t)r * kHeads + 16 * wave + i16) * kDqk;
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+            int d;
+            if (FMT == 0 || kk >= 16)
+                d = 32 * kk + 8 * g;
+            else
+                d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
+            qreg[kk] = *(const bf16x8*)(qh + d);
+        }
+    }
+    wait_vmcnt<0>();
+    // The loads above are complete; tell the compiler so it does not place
+    // vmcnt waits for them inside the loop, where the stage DMAs are in flight.
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(qreg[kk]));
+    __syncthreads();
+
+    auto issue = [&](int tile) {
+        const unsigned sbase = lds0 + (unsigned)((tile % NST) * STAGE);
+        const int t = 8 * wave + (lane >> 3);  // token of this lane within the tile
+        const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
+        const int chunk = (lane & 7) ^ swz<FMT>(t);
+        const unsigned char* src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
+        const int bstride = row >= 0 ? 128 : 0;
+#pragma unroll
+        for (int bd = 0; bd < NBANDS; ++bd)
+            lds_dma16(src + bd * bstride,
+                      __builtin_amdgcn_readfirstlane(sbase + (unsigned)((bd * kTile + 8 * wave) * 128)));
+        if (FMT == 1) {
+            // fp32 scales: lanes 0..7 fetch the 16 bytes of tokens 8*wave + lane.
+            const int t2 = 8 * wave + (lane & 7);
+            const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
+            const unsigned char* s2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
+            const unsigned dst = __builtin_amdgcn_readfirstlane(sbase + (unsigned)(NBANDS * kTile * 128 + 8 * wave * 16));
+            if (lane < 8) lds_dma16(s2, dst);
+        }
+    };
+
+    // ---- per-lane LDS byte offsets inside a stage (loop invariant); the
+    // band and token-block parts of each address are immediates.
+    // A-operand rows of S^T = K . Q^T: token tokA0 (block 0) and tokA1 (block 1).
+    // Accumulator entry j of group g: token tokC0 + j (block 0), tokC1 + j (block 1).
+    int tokA0, tokA1, tokC0, tokC1;
+    if (FMT == 0) {
+        tokA0 = i16; tokA1 = 16 + i16;
+        tokC0 = 4 * g; tokC1 = 16 + 4 * g;
+    } else {
+        tokA0 = 8 * (i16 >> 2) + (i16 & 3); tokA1 = tokA0 + 4;
+        tokC0 = 8 * g; tokC1 = 8 * g + 4;
+    }
+    // QK reads: 16 bytes of token tokA*, chunk (4*e + g) of a band (e = k-step parity / pair)
+    int qk0[2], qk1[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz<FMT>(tokA0)) << 4);
+        qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz<FMT>(tokA1)) << 4);
+    }
+    // PV transpose reads
+    //   bf16: lane i16 of group g addresses token tokC + (i16 >> 2), dims 4*(i16 & 3) of a 16-dim block;
+    //         variant m = (16-dim block index within its band)
+    //   fp8 : lane i16 of group g addresses token 8g + (i16 >> 1), 8 dims; variant = chunk of the band
+    constexpr int NPV = FMT == 0 ? 4 : 8;
+    int pv[NPV];
+    if (FMT == 0) {
+        const int ta = tokC0 + (i16 >> 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            pv[m] = ta * 128 + (((2 * m + ((i16 & 3) >> 1)) ^ swz<0>(ta)) << 4) + 8 * (i16 & 1);
+    } else {
+        const int ta = 8 * g + (i16 >> 1);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pv[c] = ta * 128 + ((c ^ swz<1>(ta)) << 4) + 8 * (i16 & 1);
+    }
+
+    f32x4 oacc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Softmax state of head 16*wave + i16: exponentials are taken against the
+    // reference m_ref, which is raised (and the accumulators rescaled) only
+    // when a tile's max exceeds it by more than kRescale, so p <= 2^kRescale.
+    constexpr float kRescale = 8.f;
+    float m_ref = -INFINITY;
+    float l_run = 0.f;  // this lane's share of sum_j p_j
+
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+        if (t < ntiles) issue(t);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int after = min(NST - 2, ntiles - 1 - it);  // tiles issued after this one
+        if (after >= 2) wait_vmcnt<2 * LPT>();
+        else if (after == 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // tile `it` is in LDS for every wave; stage (it-1)%NST is free
+        if (it + NST - 1 < ntiles) issue(it + NST - 1);
+
+        const lds_u8* st = lds + (it % NST) * STAGE;
+        const lds_u8* rt = rowtab + 4 * it * kTile;
+
+        // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        f32x4 sc0[4], sc1[4];  // fp8: sc*[j][grp] = scale of group grp of accumulator token j
+        if (FMT == 0) {
+#pragma unroll
+            for (int kk = 0; kk < 18; ++kk) {
+                const int band = kk >> 1;
+                const bf16x8 ka = lds_load<bf16x8>(st + qk0[kk & 1] + band * kTile * 128);
+                const bf16x8 kb = lds_load<bf16x8>(st + qk1[kk & 1] + band * kTile * 128);
+                s0 = mfma16(ka, qreg[kk], s0);
+                s1 = mfma16(kb, qreg[kk], s1);
+            }
+        } else {
+            const lds_u8* scl = st + NBANDS * kTile * 128;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sc0[j] = lds_load<f32x4>(scl + 16 * (tokC0 + j));
+                sc1[j] = lds_load<f32x4>(scl + 16 * (tokC1 + j));
+            }
+            // rope part: bf16 band 4, k-steps 16 and 17
+#pragma unroll
+            for (int kr = 0; kr < 2; ++kr) {
+                const bf16x8 ka = lds_load<bf16x8>(st + qk0[kr] + 4 * kTile * 128);
+                const bf16x8 kb = lds_load<bf16x8>(st + qk1[kr] + 4 * kTile * 128);
+                s0 = mfma16(ka, qreg[16 + kr], s0);
+                s1 = mfma16(kb, qreg[16 + kr], s1);
+            }
+            // c_kv part: one accumulator per 128-group, scaled per token afterwards
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                f32x4 p0 = f32x4{0.f, 0.f, 0.f, 0.f}, p1 = p0;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const u32x4 ra = lds_load<u32x4>(st + qk0[pr] + grp * kTile * 128);
+                    const u32x4 rb = lds_load<u32x4>(st + qk1[pr] + grp * kTile * 128);
+                    p0 = mfma16(e4m3x8_to_bf16(ra[0], ra[1]), qreg[4 * grp + 2 * pr], p0);
+                    p1 = mfma16(e4m3x8_to_bf16(rb[0], rb[1]), qreg[4 * grp + 2 * pr], p1);
+                    p0 = mfma16(e4m3x8_to_bf16(ra[2], ra[3]), qreg[4 * grp + 2 * pr + 1], p0);
+                    p1 = mfma16(e4m3x8_to_bf16(rb[2], rb[3]), qreg[4 * grp + 2 * pr + 1], p1);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s0[j] += sc0[j][grp] * p0[j];
+                    s1[j] += sc1[j][grp] * p1[j];
+                }
+            }
+        }
+
+        // ---- mask, online softmax (base 2)
+        const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
+        const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
+        float sv[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sv[j] = v0[j] >= 0 ? s0[j] * a.scale_log2 : -INFINITY;
+            sv[4 + j] = v1[j] >= 0 ? s1[j] * a.scale_log2 : -INFINITY;
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool raise = mx > m_ref + kRescale;  // also true for the first valid tile
+        if (__any(raise)) {
+            const float m_new = raise ? mx : m_ref;
+            const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        // The denominator sums the fp32 weights; the PV product takes them
+        // rounded to bf16.
+        bf16x8 pb;
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_use);
+            pb[j] = (__bf16)pj;
+            psum += pj;
+        }
+        l_run += psum;
+
+        // ---- O^T += V^T . P^T
+        if (FMT == 0) {
+#pragma unroll
+            for (int db = 0; db < 32; ++db) {
+                const int off = (db >> 2) * kTile * 128;
+                // (the bf16-typed form of the transpose read: rebuilding the operand
+                // element by element from the i16-typed form is miscompiled)
+                const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + off));
+                const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + off + 16 * 128));
+                const bf16x8 av = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = mfma16(av, pb, oacc[db]);
+            }
+        } else {
+            // P^T with the per-token scale of each 128-group folded in
+            bf16x8 pg[4];
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pg[grp][j] = (__bf16)((float)pb[j] * sc0[j][grp]);
+                    pg[grp][4 + j] = (__bf16)((float)pb[4 + j] * sc1[j][grp]);
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < 32; ++db) {
+                const int grp = db >> 3;
+                const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(st + pv[db & 7] + grp * kTile * 128));
+                oacc[db] = mfma16(e4m3x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]), pg[grp], oacc[db]);
+            }
+        }
+    }
+
+    // ---- epilogue: normalise, write the final result or this part's partial
+    float l_tot = l_run;
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const int h = 16 * wave + i16;
+    const bool empty = (m_ref == -INFINITY);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * kLn2;
+    if (a.num_splits == 1) {
+        uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) {
+            bf16x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(oacc[db][j] * inv);
+            *(bf16x4*)(o + 16 * db) = v;
+        }
+        if (g == 0) a.lse[(int64_t)r * kHeads + h] = lse_v;
+    } else {
+        const int64_t pr = ((int64_t)sp * a.rows + r) * kHeads + h;
+        float* o = a.part_out + pr * kDv + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) *(f32x4*)(o + 16 * db) = oacc[db] * inv;
+        if (g == 0) a.part_lse[pr] = lse_v;
+    }
+}
+
+template <int FMT>
+hipError_t launch_partial(const PartialArgs& args, int grid, size_t lds_bytes, hipStream_t stream) {
+    static std::mutex mu;
+    static bool configured[64] = {false};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (dev < 0 || dev >= 64 || !configured[dev]) {
+            e = hipFuncSetAttribute((const void*)partial_kernel<FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kLdsLimit);
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < 64) configured[dev] = true;
+        }
+    }
+    hipLaunchKernelGGL(partial_kernel<FMT>, dim3(grid), dim3(kThreads), lds_bytes, stream, args);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace smla
+
+extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q, const void* kv_cache,
+                                         int64_t num_kv_blocks, const int32_t* block_table,
+                                         const int32_t* indices, const int32_t* seq_lens, float softmax_scale,
+                                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    using namespace smla;
+    if (!plan) return SMLA_ERR_INVALID_ARG;
+    // The plan must be exactly what smla_decode_plan gives for its problem.
+    smla_plan_t check;
+    if (plan->prob.num_cus <= 0) return SMLA_ERR_INVALID_ARG;
+    smla_status_t st = smla_decode_plan(&plan->prob, &check);
+    if (st != SMLA_OK) return st;
+    if (std::memcmp(&check, plan, sizeof(check)) != 0) return SMLA_ERR_INVALID_ARG;
+    if (plan->rows == 0) return SMLA_OK;
+    if (!q || !block_table || !out || !lse) return SMLA_ERR_INVALID_ARG;
+    if (!indices && plan->prob.topk > 0) return SMLA_ERR_INVALID_ARG;
+    if (num_kv_blocks < 0 || (num_kv_blocks > 0 && !kv_cache)) return SMLA_ERR_INVALID_ARG;
+    if (num_kv_blocks > (int64_t)(INT32_MAX / kBlock)) return SMLA_ERR_UNSUPPORTED;
+    if (!std::isfinite(softmax_scale)) return SMLA_ERR_INVALID_ARG;
+    if (plan->workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan->workspace_bytes) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+        if (((uintptr_t)workspace & 255) != 0) return SMLA_ERR_INVALID_ARG;
+    }
+
+    PartialArgs args;
+    args.q = (const uint16_t*)q;
+    args.kv = (const uint8_t*)kv_cache;
+    args.block_table = block_table;
+    args.indices = indices;
+    args.seq_lens = seq_lens;
+    args.out = (uint16_t*)out;
+    args.lse = lse;
+    const int S = plan->num_splits;
+    const int64_t pairs = (int64_t)plan->rows * kHeads;
+    args.part_out = S > 1 ? (float*)workspace : nullptr;
+    args.part_lse = S > 1 ? (float*)workspace + (size_t)S * pairs * kDv : nullptr;
+    args.num_kv_blocks = num_kv_blocks;
+    args.rows = plan->rows;
+    args.q_len = plan->prob.q_len;
+    args.topk = plan->prob.topk;
+    args.max_blocks = plan->prob.max_blocks_per_seq;
+    args.tokens_per_split = plan->tokens_per_split;
+    args.num_splits = S;
+    args.scale_log2 = softmax_scale * kLog2e;
+
+    hipStream_t s = (hipStream_t)stream;
+    const size_t lds = partial_lds_bytes(plan->prob.kv_format, plan->tokens_per_split);
+    (void)hipGetLastError();  // clear an earlier, unrelated error
+    hipError_t e = plan->prob.kv_format == SMLA_KV_BF16 ? launch_partial<0>(args, plan->num_workgroups, lds, s)
+                                                        : launch_partial<1>(args, plan->num_workgroups, lds, s);
+    if (e != hipSuccess) return SMLA_ERR_LAUNCH;
+    if (S > 1) return launch_combine(args.part_out, args.part_lse, S, pairs, kDv, out, lse, s);
+    return SMLA_OK;
+}

@@ -1,0 +1,57 @@
+// Internal constants and launch-shape helpers shared by the host plan and the
+// kernels of the GPU library (not part of the public ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace smla {
+
+// The one problem shape the kernels implement.
+constexpr int kHeads = 64;       // query heads sharing one latent row
+constexpr int kDqk = 576;        // c_kv (512) + rope (64)
+constexpr int kDv = 512;         // value width = c_kv part
+constexpr int kDr = kDqk - kDv;  // rope width
+constexpr int kBlock = 64;       // tokens per cache block
+
+// Workgroup shape of the partial-attention kernel: 4 waves of 64 lanes; wave w
+// owns heads [16w, 16w + 16) for both contractions.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;        // tokens gathered per pipeline stage
+
+// Bytes of one latent row in HBM.
+constexpr int kRowBytesBf16 = 2 * kDqk;                       // 1152 = 9 x 128
+constexpr int kRowBytesFp8 = kDv + 2 * kDr + 4 * (kDv / 128); // 656 = 41 x 16
+
+// LDS image of one stage (kTile tokens).  Rows are stored as 128-byte bands:
+// band j of every token of the tile is contiguous ([band][token][128 B]), and
+// the eight 16-byte chunks inside a band are XOR-swizzled by the token index.
+//   bf16: 9 bands (576 bf16)                               -> 36864 B
+//   fp8 : 4 bands of e4m3 c_kv + 1 band of bf16 rope, then
+//         kTile x 16 B of fp32 scales                      -> 20992 B
+constexpr int kBandsBf16 = 9;
+constexpr int kBandsFp8 = 5;
+constexpr int kStageBytesBf16 = kBandsBf16 * kTile * 128;
+constexpr int kStageBytesFp8 = kBandsFp8 * kTile * 128 + kTile * 16;
+constexpr int kStagesBf16 = 3;
+constexpr int kStagesFp8 = 4;
+
+constexpr int kLdsLimit = 160 * 1024;  // bytes of LDS a gfx950 workgroup may use
+
+inline int stage_bytes(int kv_format) { return kv_format == 0 ? kStageBytesBf16 : kStageBytesFp8; }
+inline int num_stages(int kv_format) { return kv_format == 0 ? kStagesBf16 : kStagesFp8; }
+
+// LDS of one workgroup: the stage ring plus one int32 physical-row entry per
+// token of its part of the top-k list.
+inline size_t partial_lds_bytes(int kv_format, int tokens_per_split) {
+    return (size_t)num_stages(kv_format) * stage_bytes(kv_format) + 4 * (size_t)tokens_per_split;
+}
+
+// Largest part of the list (a multiple of kTile) whose row table still fits.
+inline int max_tokens_per_split(int kv_format) {
+    long room = (long)kLdsLimit - (long)num_stages(kv_format) * stage_bytes(kv_format);
+    return (int)((room / 4) / kTile * kTile);
+}
+
+}  // namespace smla

@@ -1,0 +1,137 @@
+"""The C ABI of libsmla.so without a GPU: exports, struct layout, plan logic, argument checks."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_mla_decode_smla_amd import binding as B
+from sparse_mla_decode_smla_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libsmla.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(smla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"smla_decode_plan", "smla_decode_run", "smla_combine", "smla_status_string"}
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in smla.h but not exported"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "smla.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(smla_problem_t), sizeof(smla_plan_t),
+         offsetof(smla_plan_t, rows), offsetof(smla_plan_t, num_workgroups), offsetof(smla_plan_t, workspace_bytes));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(B.Problem), ctypes.sizeof(B.Plan), B.Plan.rows.offset,
+                   B.Plan.num_workgroups.offset, B.Plan.workspace_bytes.offset]
+
+
+def test_status_strings():
+    for code in range(6):
+        assert B.status_string(code) and B.status_string(code) != "unknown status"
+    assert B.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
+def test_plan_fills_the_gpu_and_covers_the_list(w):
+    mb = (w.max_seq_len + 63) // 64
+    p = B.decode_plan(w.batch, w.q_len, w.topk, mb, w.kv_format, num_cus=256)
+    assert p.rows == w.rows
+    assert p.num_workgroups == p.rows * p.num_splits
+    assert p.tokens_per_split % p.tile_tokens == 0
+    assert (p.num_splits - 1) * p.tokens_per_split < w.topk <= p.num_splits * p.tokens_per_split
+    if p.num_splits > 1:
+        assert p.workspace_bytes == p.num_splits * p.rows * 64 * 513 * 4
+    else:
+        assert p.workspace_bytes == 0
+    # enough workgroups for every CU, unless the list has fewer tiles than that
+    tiles = -(-w.topk // p.tile_tokens)
+    assert p.num_workgroups >= min(256, p.rows * tiles) or p.num_splits == tiles
+
+
+def test_plan_is_deterministic_and_data_independent():
+    a = B.decode_plan(16, 1, 2048, 1024, num_cus=256)
+    b = B.decode_plan(16, 1, 2048, 1024, num_cus=256)
+    assert bytes(a) == bytes(b)
+
+
+def test_forced_splits_and_edge_shapes():
+    p = B.decode_plan(1, 1, 200, 8, num_cus=256, force_splits=7)
+    assert p.num_splits == 7 and p.tokens_per_split == 32
+    p = B.decode_plan(1, 1, 200, 8, num_cus=256, force_splits=1000)
+    assert p.num_splits == 7                      # never more parts than tiles
+    p = B.decode_plan(1, 1, 0, 8, num_cus=256)
+    assert p.num_splits == 1 and p.workspace_bytes == 0
+    p = B.decode_plan(0, 1, 64, 8, num_cus=256)
+    assert p.rows == 0 and p.num_workgroups == 0
+    p = B.decode_plan(1, 1, 100000, 4096, num_cus=256, force_splits=1)
+    assert p.num_splits > 1, "a part must fit the LDS row table"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=32), 2), (dict(d_qk=512), 2), (dict(d_v=448), 2), (dict(block_size=32), 2),
+    (dict(kv_format=7), 2), (dict(q_len=0), 1), (dict(topk=-1), 1), (dict(max_blocks_per_seq=0), 1),
+])
+def test_plan_rejects(kw, status):
+    args = dict(batch=2, q_len=1, topk=64, max_blocks_per_seq=8, kv_format=0, num_cus=256)
+    args.update(kw)
+    with pytest.raises(B.SmlaError) as e:
+        B.decode_plan(**args)
+    assert e.value.status == status
+
+
+def _run(plan, **kw):
+    lib = B.load()
+    args = dict(q=1 << 20, kv=1 << 21, nb=16, bt=1 << 22, idx=1 << 23, sl=None, scale=0.04, out=1 << 24,
+                lse=1 << 25, ws=None, wsb=0)
+    args.update(kw)
+    return lib.smla_decode_run(ctypes.byref(plan) if plan is not None else None, args["q"], args["kv"], args["nb"],
+                               args["bt"], args["idx"], args["sl"], args["scale"], args["out"], args["lse"],
+                               args["ws"], args["wsb"], None)
+
+
+def test_run_argument_checks_need_no_gpu():
+    plan = B.decode_plan(2, 1, 256, 8, num_cus=256)
+    assert plan.workspace_bytes > 0
+    assert _run(None) == 1
+    assert _run(plan, q=None) == 1
+    assert _run(plan, nb=-1) == 1
+    assert _run(plan, kv=None) == 1
+    assert _run(plan, scale=float("nan")) == 1
+    assert _run(plan) == 3                                   # no workspace
+    assert _run(plan, ws=1 << 26, wsb=plan.workspace_bytes - 1) == 3
+    assert _run(plan, ws=(1 << 26) + 16, wsb=plan.workspace_bytes) == 1   # misaligned
+    bad = B.Plan.from_buffer_copy(bytes(plan))
+    bad.num_splits += 1
+    assert _run(bad) == 1                                    # edited plan
+    empty = B.decode_plan(0, 1, 256, 8, num_cus=256)
+    assert _run(empty, q=None, out=None) == 0                # nothing to do
+
+
+def test_combine_argument_checks_need_no_gpu():
+    lib = B.load()
+    assert lib.smla_combine(1 << 20, 1 << 21, 0, 1, 64, 512, 1 << 22, 1 << 23, None) == 1
+    assert lib.smla_combine(1 << 20, 1 << 21, 2, 1, 64, 510, 1 << 22, 1 << 23, None) == 2
+    assert lib.smla_combine(None, None, 2, 0, 64, 512, None, None, None) == 0
+    assert lib.smla_combine(None, 1 << 21, 2, 1, 64, 512, 1 << 22, 1 << 23, None) == 1

@@ -1,0 +1,222 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Bar (fp32 accumulation of bf16 inputs): max |out - ref| <= 2e-2 and
+max |out - ref| / max |ref| <= 1e-2 over rows with a finite reference lse,
+max |lse - ref| <= 1e-3; rows with no valid index must give out = 0 and
+lse = -inf exactly.  Index handling is exact by construction (the same
+bytes go to both sides).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mla_decode_smla_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+OUT_ABS, OUT_REL, LSE_ABS = 2e-2, 1e-2, 1e-3
+
+
+def B():
+    from sparse_mla_decode_smla_amd import binding
+    return binding
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(out_gpu, lse_gpu, out_ref, lse_ref, what):
+    o = out_gpu.float().cpu().numpy().astype(np.float64)
+    lg = lse_gpu.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse_ref)
+    assert np.all(lg[~fin] == -np.inf), f"{what}: empty rows must give lse = -inf"
+    assert np.all(o[~fin] == 0.0), f"{what}: empty rows must give out = 0"
+    if not fin.any():
+        return
+    err = float(np.abs(o[fin] - out_ref[fin]).max())
+    ref_max = float(np.abs(out_ref[fin]).max())
+    lerr = float(np.abs(lg[fin] - lse_ref[fin]).max())
+    note(f"  {what}: out abs err {err:.3e} (rel {err / ref_max:.3e}), lse abs err {lerr:.3e}")
+    assert err <= OUT_ABS and err <= OUT_REL * ref_max, f"{what}: out err {err:.3e}, max|ref| {ref_max:.3e}"
+    assert lerr <= LSE_ABS, f"{what}: lse err {lerr:.3e}"
+
+
+def run_gpu(inp, indices=None, force_splits=0, with_seq_lens=True, block_table=None):
+    w = inp.workload
+    q, kv, bt, idx, sl = B().to_device(inp, indices=indices)
+    if block_table is not None:
+        bt = torch.from_numpy(block_table).cuda()
+    out, lse = B().sparse_mla_decode(q, kv, bt, idx, sl if with_seq_lens else None, inp.softmax_scale,
+                                     kv_format=w.kv_format, force_splits=force_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+FORMATS = [I.KV_BF16, I.KV_FP8]
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+def test_small_parity(fmt, splits):
+    # top-k 200 = 6 full tiles of 32 + a ragged tail of 8; q_len 2; paged, shuffled blocks
+    inp = I.small_inputs(batch=3, q_len=2, topk=200, seq_len=700, kv_format=fmt, seed=11 + fmt)
+    note(f"small parity fmt={fmt} splits={splits}")
+    ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
+    out, lse = run_gpu(inp, force_splits=splits)
+    check(out, lse, ref_o, ref_l, f"fmt{fmt} S{splits}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+def test_masking_edge_cases(fmt):
+    inp = I.small_inputs(batch=4, q_len=2, topk=100, seq_len=600, kv_format=fmt, seed=21 + fmt)
+    w = inp.workload
+    rng = np.random.default_rng(5)
+    idx = inp.indices.copy()
+    cap = 64 * inp.block_table.shape[1]
+    # row (0,0): scattered -1, negatives and positions past the table
+    pos = rng.choice(100, size=40, replace=False)
+    idx[0, 0, pos[:15]] = -1
+    idx[0, 0, pos[15:30]] = -123
+    idx[0, 0, pos[30:]] = cap + 5
+    idx[0, 1] = -1                                   # fully masked row
+    idx[1, 0] = -1
+    idx[1, 0, 57] = 333                              # a single valid index
+    idx[1, 1, :10] = idx[1, 1, 10]                   # repeated index
+    bt = inp.block_table.copy()
+    bt[2, 3] = -4                                    # bad block ids mask their positions
+    bt[3, 1] = inp.kv_cache.shape[0] + 9
+    note(f"masking edge cases fmt={fmt}")
+    ref_o, ref_l = oracle.default().sparse_mla_decode(inp.q, inp.kv_cache, bt, idx, inp.seq_lens,
+                                                      inp.softmax_scale, d_v=w.d_v, kv_format=fmt,
+                                                      block_size=64, threads=8)
+    assert np.isinf(ref_l[0, 1]).all() and np.isfinite(ref_l[1, 0]).all()
+    for splits in (0, 1, 3):
+        out, lse = run_gpu(inp, indices=idx, force_splits=splits, block_table=bt)
+        check(out, lse, ref_o, ref_l, f"masks fmt{fmt} S{splits}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+def test_seq_lens_optional(fmt):
+    inp = I.small_inputs(batch=2, q_len=1, topk=96, seq_len=256, kv_format=fmt, seed=31)
+    sl = np.array([256, 120], dtype=np.int32)
+    inp.seq_lens[:] = sl
+    ref_o, ref_l = oracle.decode_inputs(inp)
+    out, lse = run_gpu(inp)
+    check(out, lse, ref_o, ref_l, "with seq_lens")
+    ref_o2, ref_l2 = oracle.decode_inputs(inp, with_seq_lens=False)
+    out2, lse2 = run_gpu(inp, with_seq_lens=False)
+    check(out2, lse2, ref_o2, ref_l2, "without seq_lens")
+
+
+@pytest.mark.parametrize("topk", [1, 31, 33, 64])
+def test_short_lists(topk):
+    inp = I.small_inputs(batch=2, q_len=2, topk=topk, seq_len=300, kv_format=I.KV_BF16, seed=40 + topk)
+    ref_o, ref_l = oracle.decode_inputs(inp)
+    out, lse = run_gpu(inp)
+    check(out, lse, ref_o, ref_l, f"topk {topk}")
+
+
+def test_topk_zero_and_empty_batch():
+    inp = I.small_inputs(batch=2, q_len=1, topk=4, seq_len=128, kv_format=I.KV_BF16, seed=3)
+    idx0 = np.zeros((2, 1, 0), dtype=np.int32)
+    q, kv, bt, _, sl = B().to_device(inp)
+    out, lse = B().sparse_mla_decode(q, kv, bt, torch.from_numpy(idx0).cuda(), sl, inp.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    out, lse = B().sparse_mla_decode(q[:0], kv, bt[:0], torch.zeros((0, 1, 4), dtype=torch.int32).cuda(),
+                                     sl[:0], inp.softmax_scale)
+    assert out.shape[0] == 0 and lse.shape[0] == 0
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+def test_paging_invariance_bit_exact(fmt):
+    inp = I.small_inputs(batch=2, q_len=1, topk=150, seq_len=512, kv_format=fmt, seed=50)
+    w = inp.workload
+    nblk = 512 // 64
+    cache2 = np.zeros_like(inp.kv_cache)
+    bt2 = np.zeros_like(inp.block_table)
+    for b in range(2):
+        for j in range(nblk):
+            cache2[b * nblk + j] = inp.kv_cache[inp.block_table[b, j]]
+            bt2[b, j] = b * nblk + j
+    out1, lse1 = run_gpu(inp, force_splits=3)
+    inp2 = I.Inputs(**{**inp.__dict__, "kv_cache": cache2, "block_table": bt2})
+    out2, lse2 = run_gpu(inp2, force_splits=3)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_deterministic():
+    inp = I.small_inputs(batch=2, q_len=2, topk=300, seq_len=1000, kv_format=I.KV_FP8, seed=60)
+    a = run_gpu(inp, force_splits=4)
+    b = run_gpu(inp, force_splits=4)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_combine_kernel_alone():
+    rng = np.random.default_rng(70)
+    S, rows, H, dv = 5, 3, 64, 512
+    po = rng.standard_normal((S, rows, H, dv)).astype(np.float32)
+    pl = (rng.standard_normal((S, rows, H)) * 3).astype(np.float32)
+    pl[1, 0, :] = -np.inf
+    pl[:, 2, 5] = -np.inf                       # every part of one pair empty
+    ref_o, ref_l = oracle.lse_combine(po.astype(np.float64), pl.astype(np.float64))
+    out = torch.empty((rows, H, dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+    B().combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, lse)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    lg = lse.cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.all(o[~fin] == 0) and np.all(np.isneginf(lg[~fin]))
+    assert np.abs(o[fin] - ref_o[fin]).max() <= 2 ** -8 * np.abs(ref_o[fin]).max() + 1e-6
+    assert np.abs(lg[fin] - ref_l[fin]).max() <= 1e-5 * max(1.0, np.abs(ref_l[fin]).max())
+
+
+def test_runs_on_a_side_stream():
+    inp = I.small_inputs(batch=2, q_len=1, topk=128, seq_len=512, kv_format=I.KV_BF16, seed=80)
+    ref_o, ref_l = oracle.decode_inputs(inp)
+    q, kv, bt, idx, sl = B().to_device(inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = B().sparse_mla_decode(q, kv, bt, idx, sl, inp.softmax_scale)
+    s.synchronize()
+    check(out, lse, ref_o, ref_l, "side stream")
+
+
+# ---------------------------------------------------------------- full workloads
+
+@pytest.fixture(scope="module")
+def workload_cache():
+    return {}
+
+
+def _sample_rows(w, rng):
+    if w.rows <= 2:
+        return list(range(w.rows))
+    rows = sorted(set([0, w.rows - 1] + rng.choice(w.rows, size=min(4, w.rows), replace=False).tolist()))
+    return rows
+
+
+@pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
+def test_workload_parity_sampled_rows(w):
+    note(f"workload {w.name}: generating")
+    inp = I.make_inputs(w, seed=0)
+    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format)
+    note(f"workload {w.name}: plan splits={plan.num_splits} tps={plan.tokens_per_split} wgs={plan.num_workgroups}")
+    out, lse = run_gpu(inp)   # automatic plan = the launch configuration the benchmark times
+    rng = np.random.default_rng(1)
+    rows = _sample_rows(w, rng)
+    if w.name.startswith("b64"):
+        short = [int(b) for b in np.nonzero(inp.seq_lens < w.topk)[0]]
+        rows = sorted(set(rows + short[:1]))
+    bsel = sorted(set(r // w.q_len for r in rows))
+    note(f"workload {w.name}: oracle on sequences {bsel}")
+    ref_o, ref_l = oracle.default().sparse_mla_decode(
+        inp.q[bsel], inp.kv_cache, inp.block_table[bsel], inp.indices[bsel], inp.seq_lens[bsel],
+        inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format, block_size=w.block_size, threads=16)
+    check(out[bsel], lse[bsel], ref_o, ref_l, f"{w.name} sequences {bsel}")
