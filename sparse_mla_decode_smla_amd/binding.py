@@ -52,11 +52,13 @@ class Plan(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
+def load(path: Optional[str] = None):
     """Load the GPU library (raises if it is not built)."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m sparse_mla_decode_smla_amd.build` "
                            "(or __graft_entry__.build()) first")

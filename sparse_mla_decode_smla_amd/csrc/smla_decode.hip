@@ -90,16 +90,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// XOR swizzle of the eight 16-byte chunks of a band, by token.  bf16: the
-// 16-byte QK reads of 8 consecutive tokens and the 8-byte transpose reads of
-// 4 consecutive tokens both hit distinct banks.  fp8: the same for the QK
-// reads of tokens {0-3, 8-11}(+4) and the transpose reads of 8 consecutive
-// tokens.
-template <int FMT>
-__device__ __forceinline__ int swz(int t) {
-    if (FMT == 0) return ((t & 3) << 1) | ((t >> 2) & 1);
-    return (t & 3) | ((((t >> 2) ^ (t >> 3)) & 1) << 2);
-}
+// XOR swizzle of the eight 16-byte chunks of a band, by token (both cache
+// formats).  Measured free of LDS bank conflicts on gfx950 for the three read
+// shapes of the kernel: 16-byte QK reads of 16 consecutive tokens, 8-byte
+// bf16 transpose reads of 4 tokens per 16-lane group, and 8-byte fp8
+// transpose reads of tokens {4g..4g+3, 16+4g..16+4g+3} per 16-lane group g.
+__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 4) & 1); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -122,22 +118,39 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(unsigned lo, unsigned hi) {
     return r;
 }
 
+template <int N>
+__device__ __forceinline__ void wait_tiles(int after) {
+    // wait until at most `after` tiles of N DMA instructions each are still in flight
+    switch (after) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<N>(); break;
+        case 2: wait_vmcnt<2 * N>(); break;
+        case 3: wait_vmcnt<3 * N>(); break;
+        default: wait_vmcnt<4 * N>(); break;
+    }
+}
+
+
 template <int FMT>
-__global__ __launch_bounds__(kThreads, 1) void partial_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void partial_kernel(PartialArgs a) {
     constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : kStageBytesFp8;
     constexpr int NST = FMT == 0 ? kStagesBf16 : kStagesFp8;
     constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : kRowBytesFp8;
     constexpr int NBANDS = FMT == 0 ? kBandsBf16 : kBandsFp8;
     constexpr int LPT = NBANDS + (FMT == 0 ? 0 : 1);  // DMA instructions per wave per tile
+    static_assert(NST - 2 <= 4, "wait_tiles covers at most 4 tiles in flight after the current one");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_generic[];
     lds_u8* lds = (lds_u8*)smem_generic;
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
-    lds_u8* rowtab = lds + NST * STAGE;  // int32 per token of this part: physical row or -1
+    constexpr int AUX_FLAG = aux_flag_offset(FMT);
+    constexpr int AUX_DENOM = aux_denom_offset(FMT);
+    lds_u8* aux = lds + NST * STAGE;
+    lds_u8* rowtab = aux + aux_bytes(FMT);  // int32 per token of this part: physical row or -1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;    // 16-lane group
     const int i16 = lane & 15;  // lane within the group
 
@@ -147,6 +160,24 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(PartialArgs a) {
     const int k0 = sp * a.tokens_per_split;
     const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
     const int ntiles = (nk + kTile - 1) / kTile;
+
+    // ---- Q of this wave's 16 heads, as the B operand of S^T = K . Q^T.
+    // Lane (i16, g) holds head 16*wave + i16, 8 dims per k-step.  For fp8
+    // rows the c_kv dims of k-steps 2p and 2p+1 inside a 128-group are the
+    // two halves of one 16-byte run, so one LDS read feeds two k-steps.
+    bf16x8 qreg[18];
+    {
+        const uint16_t* qh = a.q + ((int64_t)r * kHeads + 16 * wave + i16) * kDqk;
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+            int d;
+            if (FMT == 0 || kk >= 16)
+                d = 32 * kk + 8 * g;
+            else
+                d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
+            qreg[kk] = *(const bf16x8*)(qh + d);
+        }
+    }
 
     // ---- logical positions -> physical rows (masked entries -> -1)
     {
@@ -166,256 +197,372 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(PartialArgs a) {
             *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
         }
     }
-
-    // ---- Q of this wave's 16 heads, as the B operand of S^T = K . Q^T.
-    // Lane (i16, g) holds head 16*wave + i16, 8 dims per k-step.  For fp8
-    // rows the c_kv dims of k-steps 2p and 2p+1 inside a 128-group are the
-    // two halves of one 16-byte run, so one LDS read feeds two k-steps.
-    bf16x8 qreg[18];
-    {
-        const uint16_t* qh = a.q + ((int64_t)r * kHeads + 16 * wave + i16) * kDqk;
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-            int d;
-            if (FMT == 0 || kk >= 16)
-                d = 32 * kk + 8 * g;
-            else
-                d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
-            qreg[kk] = *(const bf16x8*)(qh + d);
-        }
-    }
     wait_vmcnt<0>();
     // The loads above are complete; tell the compiler so it does not place
     // vmcnt waits for them inside the loop, where the stage DMAs are in flight.
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(qreg[kk]));
+    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qreg[kk]));
     __syncthreads();
 
     auto issue = [&](int tile) {
         const unsigned sbase = lds0 + (unsigned)((tile % NST) * STAGE);
         const int t = 8 * wave + (lane >> 3);  // token of this lane within the tile
         const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
-        const int chunk = (lane & 7) ^ swz<FMT>(t);
+        const int chunk = (lane & 7) ^ swz(t);
         const unsigned char* src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
         const int bstride = row >= 0 ? 128 : 0;
 #pragma unroll
         for (int bd = 0; bd < NBANDS; ++bd)
-            lds_dma16(src + bd * bstride,
-                      __builtin_amdgcn_readfirstlane(sbase + (unsigned)((bd * kTile + 8 * wave) * 128)));
+            lds_dma16(src + bd * bstride, sbase + (unsigned)((bd * kTile + 8 * wave) * 128));
         if (FMT == 1) {
             // fp32 scales: lanes 0..7 fetch the 16 bytes of tokens 8*wave + lane.
             const int t2 = 8 * wave + (lane & 7);
             const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
             const unsigned char* s2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
-            const unsigned dst = __builtin_amdgcn_readfirstlane(sbase + (unsigned)(NBANDS * kTile * 128 + 8 * wave * 16));
+            const unsigned dst = sbase + (unsigned)(NBANDS * kTile * 128 + 8 * wave * 16);
             if (lane < 8) lds_dma16(s2, dst);
         }
     };
 
-    // ---- per-lane LDS byte offsets inside a stage (loop invariant); the
-    // band and token-block parts of each address are immediates.
+    // ---- per-lane LDS byte offsets inside a stage (loop invariant)
     // A-operand rows of S^T = K . Q^T: token tokA0 (block 0) and tokA1 (block 1).
     // Accumulator entry j of group g: token tokC0 + j (block 0), tokC1 + j (block 1).
-    int tokA0, tokA1, tokC0, tokC1;
-    if (FMT == 0) {
-        tokA0 = i16; tokA1 = 16 + i16;
-        tokC0 = 4 * g; tokC1 = 16 + 4 * g;
-    } else {
-        tokA0 = 8 * (i16 >> 2) + (i16 & 3); tokA1 = tokA0 + 4;
-        tokC0 = 8 * g; tokC1 = 8 * g + 4;
-    }
+    const int tokA0 = i16, tokA1 = 16 + i16;
+    const int tokC0 = 4 * g, tokC1 = 16 + 4 * g;
     // QK reads: 16 bytes of token tokA*, chunk (4*e + g) of a band (e = k-step parity / pair)
     int qk0[2], qk1[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz<FMT>(tokA0)) << 4);
-        qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz<FMT>(tokA1)) << 4);
+        qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz(tokA0)) << 4);
+        qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz(tokA1)) << 4);
     }
-    // PV transpose reads
-    //   bf16: lane i16 of group g addresses token tokC + (i16 >> 2), dims 4*(i16 & 3) of a 16-dim block;
-    //         variant m = (16-dim block index within its band)
-    //   fp8 : lane i16 of group g addresses token 8g + (i16 >> 1), 8 dims; variant = chunk of the band
-    constexpr int NPV = FMT == 0 ? 4 : 8;
-    int pv[NPV];
+    // PV transpose reads of this wave's 128 value dims [128*wave, 128*wave + 128):
+    //   bf16: lane i16 of group g addresses token tokC + (i16 >> 2), 4 dims at 4*(i16 & 3)
+    //         of a 16-dim block; variant m = block index within its 64-dim band
+    //   fp8 : lane i16 of group g addresses token T = tokC0 + j or tokC1 + j - 4 (j = i16 >> 1),
+    //         8 dims at 8*(i16 & 1) of a 16-dim block; out of the 8-bit transpose read,
+    //         k-slot 8g + j is that token, matching P^T; the wave's dims are band
+    //         (= scale group) `wave`
+    // (bf16: entries 0-3 for the tokens of block 0, 4-7 for block 1)
+    int pv[8];
     if (FMT == 0) {
-        const int ta = tokC0 + (i16 >> 2);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            pv[m] = ta * 128 + (((2 * m + ((i16 & 3) >> 1)) ^ swz<0>(ta)) << 4) + 8 * (i16 & 1);
+        for (int blk = 0; blk < 2; ++blk) {
+            const int ta = (blk == 0 ? tokC0 : tokC1) + (i16 >> 2);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                pv[4 * blk + m] = (2 * wave * kTile + ta) * 128 + (((2 * m + ((i16 & 3) >> 1)) ^ swz(ta)) << 4) +
+                                  8 * (i16 & 1);
+        }
     } else {
-        const int ta = 8 * g + (i16 >> 1);
+        const int j = i16 >> 1;
+        const int ta = j < 4 ? tokC0 + j : tokC1 + (j - 4);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) pv[c] = ta * 128 + ((c ^ swz<1>(ta)) << 4) + 8 * (i16 & 1);
+        for (int c = 0; c < 8; ++c)
+            pv[c] = (wave * kTile + ta) * 128 + ((c ^ swz(ta)) << 4) + 8 * (i16 & 1);
     }
 
-    f32x4 oacc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Softmax state of head 16*wave + i16: exponentials are taken against the
-    // reference m_ref, which is raised (and the accumulators rescaled) only
-    // when a tile's max exceeds it by more than kRescale, so p <= 2^kRescale.
-    constexpr float kRescale = 8.f;
+    lds_u8* const p_mine = aux + (wave * 64 + lane) * 16;  // + grp * kPBytesPerCopy for fp8
+
+    // Softmax state of head 16*wave + i16.  Exponentials are taken against a
+    // reference fixed at the first tile with a valid token (that tile's max),
+    // so the accumulators are never rescaled inside the loop; weights up to
+    // 2^kMaxRise stay finite in fp32 and bf16.  If a later score rises above
+    // the reference by more than that, the workgroup restarts its part of
+    // the list with the reference raised to that tile's max (the row table
+    // and Q stay; the accumulators of the abandoned pass are discarded).
+    constexpr float kMaxRise = 64.f;
     float m_ref = -INFINITY;
-    float l_run = 0.f;  // this lane's share of sum_j p_j
+    float l_run;        // this lane's share of sum_j p_j
+    f32x4 oacc[8][4];   // O^T of this wave: [16-dim block of its 128 dims][16-head block]
 
+    for (;;) {
 #pragma unroll
-    for (int t = 0; t < NST - 1; ++t)
-        if (t < ntiles) issue(t);
-
-    for (int it = 0; it < ntiles; ++it) {
-        const int after = min(NST - 2, ntiles - 1 - it);  // tiles issued after this one
-        if (after >= 2) wait_vmcnt<2 * LPT>();
-        else if (after == 1) wait_vmcnt<LPT>();
-        else wait_vmcnt<0>();
-        __syncthreads();  // tile `it` is in LDS for every wave; stage (it-1)%NST is free
-        if (it + NST - 1 < ntiles) issue(it + NST - 1);
-
-        const lds_u8* st = lds + (it % NST) * STAGE;
-        const lds_u8* rt = rowtab + 4 * it * kTile;
-
-        // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
-        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        f32x4 sc0[4], sc1[4];  // fp8: sc*[j][grp] = scale of group grp of accumulator token j
-        if (FMT == 0) {
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int kk = 0; kk < 18; ++kk) {
-                const int band = kk >> 1;
-                const bf16x8 ka = lds_load<bf16x8>(st + qk0[kk & 1] + band * kTile * 128);
-                const bf16x8 kb = lds_load<bf16x8>(st + qk1[kk & 1] + band * kTile * 128);
-                s0 = mfma16(ka, qreg[kk], s0);
-                s1 = mfma16(kb, qreg[kk], s1);
+            for (int hb = 0; hb < 4; ++hb) {
+                oacc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // the accumulators live in AGPRs from the start, so the loop
+                // does not move them between register files each iteration
+                asm volatile("" : "+a"(oacc[i][hb]));
             }
-        } else {
-            const lds_u8* scl = st + NBANDS * kTile * 128;
+        l_run = 0.f;
+        bool have_ref = m_ref != -INFINITY;  // set by an earlier pass
+        bool restart = false;
+
+#pragma unroll
+        for (int t = 0; t < NST - 1; ++t)
+            if (t < ntiles) issue(t);
+
+        for (int it = 0; it < ntiles; ++it) {
+            wait_tiles<LPT>(min(NST - 2, ntiles - 1 - it));
+            __syncthreads();  // tile `it` is in LDS for every wave; stage (it-1)%NST is free
+            if (it + NST - 1 < ntiles) issue(it + NST - 1);
+
+            const lds_u8* st = lds + (it % NST) * STAGE;
+            const lds_u8* rt = rowtab + 4 * it * kTile;
+            // validity of the accumulator tokens (row table entry >= 0)
+            const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
+            const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
+
+            // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
+            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+            f32x4 sc0[4], sc1[4];  // fp8: sc*[j][grp] = scale of group grp of accumulator token j
+            if (FMT == 0) {
+                constexpr int PF = 6;  // k-steps of K operands in flight
+                bf16x8 ka[PF], kb[PF];
+#pragma unroll
+                for (int kk = 0; kk < PF; ++kk) {
+                    ka[kk] = lds_load<bf16x8>(st + qk0[kk & 1] + (kk >> 1) * kTile * 128);
+                    kb[kk] = lds_load<bf16x8>(st + qk1[kk & 1] + (kk >> 1) * kTile * 128);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 18; ++kk) {
+                    const int sl = kk % PF;
+                    s0 = mfma16(ka[sl], qreg[kk], s0);
+                    s1 = mfma16(kb[sl], qreg[kk], s1);
+                    if (kk + PF < 18) {
+                        const int kn = kk + PF;
+                        ka[sl] = lds_load<bf16x8>(st + qk0[kn & 1] + (kn >> 1) * kTile * 128);
+                        kb[sl] = lds_load<bf16x8>(st + qk1[kn & 1] + (kn >> 1) * kTile * 128);
+                    }
+                }
+                // keep 2*PF reads in flight: PF pairs of reads first, then MFMA pair / read pair
+#pragma unroll
+                for (int i = 0; i < 2 * PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < 18 - PF; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+            } else {
+                // 10 load units per block: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
+                constexpr int PF = 5;
+                u32x4 ka[PF], kb[PF];
+                auto unit_off = [&](int u, int blk) {
+                    const int* qo = blk == 0 ? qk0 : qk1;
+                    return u < 2 ? qo[u] + 4 * kTile * 128 : qo[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
+                };
+                const lds_u8* scl = st + NBANDS * kTile * 128;
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
+                    kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc0[j] = lds_load<f32x4>(scl + 16 * (tokC0 + j));
+                    sc1[j] = lds_load<f32x4>(scl + 16 * (tokC1 + j));
+                }
+                f32x4 p0 = s0, p1 = s0;
+#pragma unroll
+                for (int u = 0; u < 10; ++u) {
+                    const int sl = u % PF;
+                    if (u < 2) {
+                        s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[16 + u], s0);
+                        s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[16 + u], s1);
+                    } else {
+                        const int grp = (u - 2) >> 1, pr = (u - 2) & 1;
+                        if (pr == 0) { p0 = f32x4{0.f, 0.f, 0.f, 0.f}; p1 = p0; }
+                        p0 = mfma16(e4m3x8_to_bf16(ka[sl][0], ka[sl][1]), qreg[4 * grp + 2 * pr], p0);
+                        p1 = mfma16(e4m3x8_to_bf16(kb[sl][0], kb[sl][1]), qreg[4 * grp + 2 * pr], p1);
+                        p0 = mfma16(e4m3x8_to_bf16(ka[sl][2], ka[sl][3]), qreg[4 * grp + 2 * pr + 1], p0);
+                        p1 = mfma16(e4m3x8_to_bf16(kb[sl][2], kb[sl][3]), qreg[4 * grp + 2 * pr + 1], p1);
+                        if (pr == 1) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                s0[j] += sc0[j][grp] * p0[j];
+                                s1[j] += sc1[j][grp] * p1[j];
+                            }
+                        }
+                    }
+                    if (u + PF < 10) {
+                        ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
+                        kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
+                    }
+                }
+                // first PF units' reads and the scales, then per unit its MFMAs and the next unit's reads
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF + 8, 0);
+#pragma unroll
+                for (int u = 0; u < 10 - PF; ++u) {
+                    if (u < 2)
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    else
+                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+            }
+
+            // ---- mask, softmax weights (base 2) for this wave's heads
+            float sv[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sc0[j] = lds_load<f32x4>(scl + 16 * (tokC0 + j));
-                sc1[j] = lds_load<f32x4>(scl + 16 * (tokC1 + j));
+                sv[j] = v0[j] >= 0 ? s0[j] * a.scale_log2 : -INFINITY;
+                sv[4 + j] = v1[j] >= 0 ? s1[j] * a.scale_log2 : -INFINITY;
             }
-            // rope part: bf16 band 4, k-steps 16 and 17
+            bool rise = false;
+            if (!have_ref) {
+                // first tile with a valid token (the same tile for every head and wave)
+                const bool any_valid = v0[0] >= 0 || v0[1] >= 0 || v0[2] >= 0 || v0[3] >= 0 || v1[0] >= 0 ||
+                                       v1[1] >= 0 || v1[2] >= 0 || v1[3] >= 0;
+                if (__any(any_valid)) {
+                    float mx = sv[0];
 #pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
-                const bf16x8 ka = lds_load<bf16x8>(st + qk0[kr] + 4 * kTile * 128);
-                const bf16x8 kb = lds_load<bf16x8>(st + qk1[kr] + 4 * kTile * 128);
-                s0 = mfma16(ka, qreg[16 + kr], s0);
-                s1 = mfma16(kb, qreg[16 + kr], s1);
-            }
-            // c_kv part: one accumulator per 128-group, scaled per token afterwards
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                f32x4 p0 = f32x4{0.f, 0.f, 0.f, 0.f}, p1 = p0;
-#pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    const u32x4 ra = lds_load<u32x4>(st + qk0[pr] + grp * kTile * 128);
-                    const u32x4 rb = lds_load<u32x4>(st + qk1[pr] + grp * kTile * 128);
-                    p0 = mfma16(e4m3x8_to_bf16(ra[0], ra[1]), qreg[4 * grp + 2 * pr], p0);
-                    p1 = mfma16(e4m3x8_to_bf16(rb[0], rb[1]), qreg[4 * grp + 2 * pr], p1);
-                    p0 = mfma16(e4m3x8_to_bf16(ra[2], ra[3]), qreg[4 * grp + 2 * pr + 1], p0);
-                    p1 = mfma16(e4m3x8_to_bf16(rb[2], rb[3]), qreg[4 * grp + 2 * pr + 1], p1);
+                    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+                    mx = fmaxf(mx, __shfl_xor(mx, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    m_ref = mx;
+                    have_ref = true;
                 }
+            } else {
+                float mx = sv[0];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    s0[j] += sc0[j][grp] * p0[j];
-                    s1[j] += sc1[j][grp] * p1[j];
+                for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+                if (mx > m_ref + kMaxRise) {  // lane-local test; the restart is decided after PV
+                    rise = true;
+                    m_ref = fmaxf(m_ref, mx);  // (lanes of one head reconcile below, on restart)
                 }
             }
-        }
+            const float m_use = have_ref ? m_ref : 0.f;
+            // The denominator sums the fp32 weights; the PV product takes them
+            // rounded to bf16 once (for fp8 rows after multiplying by the
+            // token's scale of each 128-group, one copy per group).
+            float pf[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pf[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
+                psum += pf[j];
+            }
+            l_run += psum;
+            if (FMT == 0) {
+                bf16x8 pb;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pb[j] = (__bf16)pf[j];
+                *(__attribute__((address_space(3))) bf16x8*)p_mine = pb;
+            } else {
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    bf16x8 pg;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pg[j] = (__bf16)(pf[j] * sc0[j][grp]);
+                        pg[4 + j] = (__bf16)(pf[4 + j] * sc1[j][grp]);
+                    }
+                    *(__attribute__((address_space(3))) bf16x8*)(p_mine + grp * kPBytesPerCopy) = pg;
+                }
+            }
+            const int any_rise = __any(rise) ? 1 : 0;
+            if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 4 * wave) = any_rise;
+            __syncthreads();  // P and the rise flags of every wave are visible
+            const i32x4 flags = lds_load<i32x4>(aux + AUX_FLAG);
 
-        // ---- mask, online softmax (base 2)
-        const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
-        const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
-        float sv[8];
+            // ---- O^T[this wave's dims, all heads] += V^T . P^T
+            bf16x8 pbh[4];  // P^T of head block hb (for fp8 rows: scaled for this wave's group)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sv[j] = v0[j] >= 0 ? s0[j] * a.scale_log2 : -INFINITY;
-            sv[4 + j] = v1[j] >= 0 ? s1[j] * a.scale_log2 : -INFINITY;
-        }
-        float mx = sv[0];
+            for (int hb = 0; hb < 4; ++hb)
+                pbh[hb] = lds_load<bf16x8>(aux + (FMT == 0 ? 0 : wave * kPBytesPerCopy) + (hb * 64 + lane) * 16);
+            if (FMT == 0) {
+                constexpr int PF = 3;  // 16-dim blocks of transpose reads in flight
+                bf16x4 va[PF], vb[PF];
+                auto tr = [&](int db, int blk) {
+                    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4*)(st + pv[4 * blk + (db & 3)] + (db >> 2) * kTile * 128));
+                };
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool raise = mx > m_ref + kRescale;  // also true for the first valid tile
-        if (__any(raise)) {
-            const float m_new = raise ? mx : m_ref;
-            const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            l_run *= alpha;
+                for (int db = 0; db < PF; ++db) { va[db] = tr(db, 0); vb[db] = tr(db, 1); }
 #pragma unroll
-            for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
-            m_ref = m_new;
-        }
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        // The denominator sums the fp32 weights; the PV product takes them
-        // rounded to bf16.
-        bf16x8 pb;
-        float psum = 0.f;
+                for (int db = 0; db < 8; ++db) {
+                    const int sl = db % PF;
+                    // (the bf16-typed transpose read: rebuilding the operand element
+                    // by element from the i16-typed form is miscompiled)
+                    const bf16x8 av = __builtin_shufflevector(va[sl], vb[sl], 0, 1, 2, 3, 4, 5, 6, 7);
+                    if (db + PF < 8) { va[sl] = tr(db + PF, 0); vb[sl] = tr(db + PF, 1); }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_use);
-            pb[j] = (__bf16)pj;
-            psum += pj;
-        }
-        l_run += psum;
-
-        // ---- O^T += V^T . P^T
-        if (FMT == 0) {
-#pragma unroll
-            for (int db = 0; db < 32; ++db) {
-                const int off = (db >> 2) * kTile * 128;
-                // (the bf16-typed form of the transpose read: rebuilding the operand
-                // element by element from the i16-typed form is miscompiled)
-                const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + off));
-                const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + off + 16 * 128));
-                const bf16x8 av = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = mfma16(av, pb, oacc[db]);
-            }
-        } else {
-            // P^T with the per-token scale of each 128-group folded in
-            bf16x8 pg[4];
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pg[grp][j] = (__bf16)((float)pb[j] * sc0[j][grp]);
-                    pg[grp][4 + j] = (__bf16)((float)pb[4 + j] * sc1[j][grp]);
+                    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
                 }
-            }
+                // P^T and the first PF blocks' reads, then per block 4 MFMAs and the next block's reads
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PF, 0);
 #pragma unroll
-            for (int db = 0; db < 32; ++db) {
-                const int grp = db >> 3;
-                const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) i32x2*)(st + pv[db & 7] + grp * kTile * 128));
-                oacc[db] = mfma16(e4m3x8_to_bf16((unsigned)raw[0], (unsigned)raw[1]), pg[grp], oacc[db]);
+                for (int db = 0; db < 8 - PF; ++db) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+            } else {
+                constexpr int PF = 4;
+                i32x2 raw[PF];
+                auto tr = [&](int db) {
+                    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(st + pv[db]));
+                };
+#pragma unroll
+                for (int db = 0; db < PF; ++db) raw[db] = tr(db);
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const int sl = db % PF;
+                    const bf16x8 av = e4m3x8_to_bf16((unsigned)raw[sl][0], (unsigned)raw[sl][1]);
+                    if (db + PF < 8) raw[sl] = tr(db + PF);
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 + PF, 0);
+#pragma unroll
+                for (int db = 0; db < 8 - PF; ++db) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+            }
+
+            if (flags[0] | flags[1] | flags[2] | flags[3]) {  // rare: restart with raised references
+                restart = true;
+                break;
             }
         }
+        if (!restart) break;
+        m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 16));  // the four lanes of a head agree
+        m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 32));
+        wait_vmcnt<0>();   // drain the stage DMAs still in flight
+        __syncthreads();   // every wave has left the loop before stages are refilled
     }
 
     // ---- epilogue: normalise, write the final result or this part's partial
     float l_tot = l_run;
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    const int h = 16 * wave + i16;
     const bool empty = (m_ref == -INFINITY);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * kLn2;
-    if (a.num_splits == 1) {
-        uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 4 * g;
+    if (g == 0) {
+        const int h = 16 * wave + i16;
+        *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * h) = empty ? 0.f : l_tot;
+        const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * kLn2;
+        if (a.num_splits == 1)
+            a.lse[(int64_t)r * kHeads + h] = lse_v;
+        else
+            a.part_lse[((int64_t)sp * a.rows + r) * kHeads + h] = lse_v;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int db = 0; db < 32; ++db) {
-            bf16x4 v;
+    for (int hb = 0; hb < 4; ++hb) {
+        const int h = 16 * hb + i16;
+        const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h);
+        const float inv = lt == 0.f ? 0.f : 1.f / lt;
+        if (a.num_splits == 1) {
+            uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 128 * wave + 4 * g;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (__bf16)(oacc[db][j] * inv);
-            *(bf16x4*)(o + 16 * db) = v;
+            for (int db = 0; db < 8; ++db) {
+                bf16x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = (__bf16)(oacc[db][hb][j] * inv);
+                *(bf16x4*)(o + 16 * db) = v;
+            }
+        } else {
+            float* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 128 * wave + 4 * g;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = oacc[db][hb] * inv;
         }
-        if (g == 0) a.lse[(int64_t)r * kHeads + h] = lse_v;
-    } else {
-        const int64_t pr = ((int64_t)sp * a.rows + r) * kHeads + h;
-        float* o = a.part_out + pr * kDv + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 32; ++db) *(f32x4*)(o + 16 * db) = oacc[db] * inv;
-        if (g == 0) a.part_lse[pr] = lse_v;
     }
 }
 

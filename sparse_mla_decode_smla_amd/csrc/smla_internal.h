@@ -34,23 +34,33 @@ constexpr int kBandsBf16 = 9;
 constexpr int kBandsFp8 = 5;
 constexpr int kStageBytesBf16 = kBandsBf16 * kTile * 128;
 constexpr int kStageBytesFp8 = kBandsFp8 * kTile * 128 + kTile * 16;
-constexpr int kStagesBf16 = 3;
-constexpr int kStagesFp8 = 4;
+constexpr int kStagesBf16 = 4;
+constexpr int kStagesFp8 = 6;
+
+// Exchange area after the stage ring: the softmax weights P of each wave's
+// 16 heads in MFMA operand order (64 lanes x 16 B per wave; for fp8 rows one
+// copy per 128-group with that group's per-token scale folded in), the
+// per-wave restart flags and the per-head softmax denominators.
+constexpr int kPBytesPerCopy = kWaves * 64 * 16;
+inline constexpr int aux_p_bytes(int kv_format) { return kv_format == 0 ? kPBytesPerCopy : 4 * kPBytesPerCopy; }
+inline constexpr int aux_flag_offset(int kv_format) { return aux_p_bytes(kv_format); }
+inline constexpr int aux_denom_offset(int kv_format) { return aux_p_bytes(kv_format) + 64; }
+inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + kHeads * 4; }
 
 constexpr int kLdsLimit = 160 * 1024;  // bytes of LDS a gfx950 workgroup may use
 
 inline int stage_bytes(int kv_format) { return kv_format == 0 ? kStageBytesBf16 : kStageBytesFp8; }
 inline int num_stages(int kv_format) { return kv_format == 0 ? kStagesBf16 : kStagesFp8; }
 
-// LDS of one workgroup: the stage ring plus one int32 physical-row entry per
-// token of its part of the top-k list.
+// LDS of one workgroup: the stage ring, the exchange area, and one int32
+// physical-row entry per token of its part of the top-k list.
 inline size_t partial_lds_bytes(int kv_format, int tokens_per_split) {
-    return (size_t)num_stages(kv_format) * stage_bytes(kv_format) + 4 * (size_t)tokens_per_split;
+    return (size_t)num_stages(kv_format) * stage_bytes(kv_format) + aux_bytes(kv_format) + 4 * (size_t)tokens_per_split;
 }
 
 // Largest part of the list (a multiple of kTile) whose row table still fits.
 inline int max_tokens_per_split(int kv_format) {
-    long room = (long)kLdsLimit - (long)num_stages(kv_format) * stage_bytes(kv_format);
+    long room = (long)kLdsLimit - (long)num_stages(kv_format) * stage_bytes(kv_format) - aux_bytes(kv_format);
     return (int)((room / 4) / kTile * kTile);
 }
 

@@ -132,13 +132,14 @@ def _e4m3fn_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def _row_values(w: Workload, rng: np.random.Generator, n: int) -> np.ndarray:
-    """Bytes of n token rows, uint8 [n, row_bytes]."""
+def encode_rows(w: Workload, values: np.ndarray) -> np.ndarray:
+    """Cache bytes uint8 [n, row_bytes] of float32 latent rows [n, d_qk] in the workload's format."""
+    values = np.ascontiguousarray(values, dtype=np.float32)
+    n = values.shape[0]
     if w.kv_format == KV_BF16:
-        vals = bf16_bits_rne(rng.standard_normal((n, w.d_qk), dtype=np.float32))
-        return vals.view(np.uint8).reshape(n, w.row_bytes)
-    c = rng.standard_normal((n, w.d_v), dtype=np.float32)
-    rope = bf16_bits_rne(rng.standard_normal((n, w.d_qk - w.d_v), dtype=np.float32))
+        return bf16_bits_rne(values).view(np.uint8).reshape(n, w.row_bytes)
+    c = values[:, : w.d_v]
+    rope = bf16_bits_rne(values[:, w.d_v:])
     groups = c.reshape(n, w.d_v // 128, 128)
     amax = np.abs(groups).max(axis=2)
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
@@ -148,6 +149,15 @@ def _row_values(w: Workload, rng: np.random.Generator, n: int) -> np.ndarray:
     out[:, w.d_v: w.d_v + 2 * (w.d_qk - w.d_v)] = rope.view(np.uint8).reshape(n, -1)
     out[:, w.d_v + 2 * (w.d_qk - w.d_v):] = scale.view(np.uint8).reshape(n, -1)
     return out
+
+
+def _row_values(w: Workload, rng: np.random.Generator, n: int) -> np.ndarray:
+    """Bytes of n token rows, uint8 [n, row_bytes]."""
+    if w.kv_format == KV_BF16:
+        return encode_rows(w, rng.standard_normal((n, w.d_qk), dtype=np.float32))
+    c = rng.standard_normal((n, w.d_v), dtype=np.float32)
+    rope = rng.standard_normal((n, w.d_qk - w.d_v), dtype=np.float32)
+    return encode_rows(w, np.concatenate([c, rope], axis=1))
 
 
 def _index_set(w: Workload, rng: np.random.Generator, seq_lens: np.ndarray) -> np.ndarray:

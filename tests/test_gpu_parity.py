@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_pins
 from sparse_mla_decode_smla_amd import inputs as I
 
 torch = pytest.importorskip("torch")
@@ -111,6 +112,31 @@ def test_seq_lens_optional(fmt):
     ref_o2, ref_l2 = oracle.decode_inputs(inp, with_seq_lens=False)
     out2, lse2 = run_gpu(inp, with_seq_lens=False)
     check(out2, lse2, ref_o2, ref_l2, "without seq_lens")
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+def test_late_large_scores_restart(fmt):
+    # A token near the end of each list gets a score far above the first tiles' max
+    # (the rope part of its K row is a large multiple of head 0's rope query; its V
+    # part stays as generated), so the kernel must raise its softmax reference after
+    # accumulating; forced splits keep several tiles per part.
+    inp = I.small_inputs(batch=2, q_len=1, topk=256, seq_len=512, kv_format=fmt, seed=90)
+    w = inp.workload
+    kv = inp.kv_cache.reshape(-1, w.row_bytes).copy()
+    for b in range(2):
+        p = int(inp.indices[b, 0, 250])
+        row = int(inp.block_table[b, p // 64]) * 64 + p % 64
+        qf = (inp.q[b, 0, 0].astype(np.uint32) << 16).view(np.float32)
+        kf = oracle_pins.token_rows(inp, b, np.array([p]))[0].astype(np.float32)
+        kf[w.d_v:] = qf[w.d_v:] * np.float32(60.0)
+        kv[row] = I.encode_rows(w, kf[None, :])[0]
+    inp2 = I.Inputs(**{**inp.__dict__, "kv_cache": kv.reshape(inp.kv_cache.shape)})
+    ref_o, ref_l = oracle.decode_inputs(inp2)
+    # head 0 must sit far (> 64 in log2 units) above the first tiles: about 130 nats here
+    assert ref_l[:, 0, 0].min() > 100, "the planted token must dominate head 0"
+    for splits in (1, 2):
+        out, lse = run_gpu(inp2, force_splits=splits)
+        check(out, lse, ref_o, ref_l, f"late large score S{splits}")
 
 
 @pytest.mark.parametrize("topk", [1, 31, 33, 64])
