@@ -16,9 +16,10 @@ so a step's rows are not still cached from the previous visit.
 
 Output: one JSON line.  ``value`` = gathered-KV GB/s of the whole call
 (gathered bytes = valid selected tokens * row bytes).  ``roofline`` is for
-the partial-attention kernel alone: its time is the graph time per call minus
-the combine kernel's time (timed the same way on the same partials).
-``cpu_baseline`` times the fp64 oracle on the host for a bounded sample.
+the partial-attention kernel alone, timed the same way from a graph of K
+``smla_decode_partial`` calls (the combine kernel is timed from a graph of
+K ``smla_combine`` calls).  ``cpu_baseline`` times the fp64 oracle on the
+host for a bounded sample.
 """
 from __future__ import annotations
 
@@ -69,6 +70,70 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+PARTIAL_KERNEL = "partial_kernel"
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe() -> int:
+    """A plain streaming kernel of known size (reads and writes COPY_PROBE_BYTES each) to scale counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": "bitwise_not uint8", "bytes_read": COPY_PROBE_BYTES,
+                      "bytes_written": COPY_PROBE_BYTES}), flush=True)
+    return 0
+
+
+def _counter_means(csv_dir: str, counter: str, name_part: str) -> tuple[float, int]:
+    """Mean per-dispatch value of `counter` over dispatches whose kernel name contains `name_part`."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {csv_dir}")
+    per_dispatch = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    key = (f, r["Dispatch_Id"])
+                    per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise ValueError(f"no {counter} rows for kernels matching {name_part!r} under {csv_dir}")
+    vals = list(per_dispatch.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                    copy_write_dir: str, command: str) -> int:
+    """Turn FETCH_SIZE / WRITE_SIZE counter runs (KiB per dispatch) into HBM bytes per partial launch."""
+    fetch_kib, nf = _counter_means(fetch_dir, "FETCH_SIZE", PARTIAL_KERNEL)
+    write_kib, nw = _counter_means(write_dir, "WRITE_SIZE", PARTIAL_KERNEL)
+    cf_kib, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "elementwise")
+    cw_kib, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "elementwise")
+    f_scale = COPY_PROBE_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_PROBE_BYTES / (cw_kib * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    rec = {"workload": workload, "kernel": PARTIAL_KERNEL, "kernel_source_hash": kernel_source_hash(),
+           "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+           "bytes_per_launch": round(fetch_b + write_b), "dispatches": {"fetch": nf, "write": nw},
+           "raw_kib_per_dispatch": {"FETCH_SIZE": fetch_kib, "WRITE_SIZE": write_kib},
+           "copy_probe": {"bytes": COPY_PROBE_BYTES, "FETCH_SIZE_kib": cf_kib, "WRITE_SIZE_kib": cw_kib,
+                          "fetch_scale": f_scale, "write_scale": w_scale},
+           "command": command}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
     import oracle
     w = inp.workload
@@ -88,7 +153,7 @@ def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
-    sample_bytes = inp.valid_count(inp.indices[sel]) * w.row_bytes * reps
+    sample_bytes = inp.valid_count(inp.indices[sel], inp.seq_lens[sel]) * w.row_bytes * reps
     return {"value": round(sample_bytes / el / 1e9, 6), "unit": "GB/s", "cores": min(threads, rows),
             "kind": "oracle",
             "sample": f"{reps} x {nseq} sequence(s) ({rows} query rows, all 64 heads) of the workload, "
@@ -104,12 +169,23 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=0, help="override the planned split count (sweeps)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain streaming kernel of known size (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                            "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc csv output directories")
+    ap.add_argument("--traffic-command", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        return traffic_summary(args.workload, *args.traffic_summary, command=args.traffic_command)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
+    if args.copy_probe:
+        return copy_probe()
 
     import numpy as np
     import torch
@@ -141,6 +217,9 @@ def main() -> int:
     def step(i):
         B.decode_run(plan, q, copies[i % R], bt, idx, sl, scale, out, lse, ws)
 
+    def step_partial(i):
+        B.decode_partial(plan, q, copies[i % R], bt, idx, sl, scale, out, lse, ws)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -158,52 +237,45 @@ def main() -> int:
 
     K = args.steps
     stream = torch.cuda.Stream(device=dev)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(K):
+                    fn(i)
+        return g
+
+    def time_graph(g) -> float:
+        """us per step of one replay of K captured steps, timed on the capture stream."""
+        g.replay()  # warm replay
         torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(K):
-                step(i)
+        with torch.cuda.stream(stream):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            g.replay()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) * 1e3 / K
+
+    graph = capture(step)
     graph.replay()
     torch.cuda.synchronize()
     if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
         log("[bench] graph replay result differs from the eager result")
         return 1
+    call_us = time_graph(graph)
+    del graph
 
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        graph.replay()
-        s1.record(stream)
-    torch.cuda.synchronize()
-    call_us = s0.elapsed_time(s1) * 1e3 / K
-
-    # combine kernel alone, on the same partials, same way
+    # the partial-attention kernel alone (the dominant kernel), then the combine alone
+    partial_us = time_graph(capture(step_partial))
     combine_us = 0.0
     if plan.num_splits > 1:
-        S, rows = plan.num_splits, plan.rows
-        pairs = rows * w.num_heads
-        part_out = ws[: S * pairs * w.d_v * 4].view(torch.float32).view(S, rows, w.num_heads, w.d_v)
-        part_lse = ws[S * pairs * w.d_v * 4: S * pairs * (w.d_v + 1) * 4].view(torch.float32).view(
-            S, rows, w.num_heads)
-        out2 = torch.empty_like(out).view(rows, w.num_heads, w.d_v)
-        lse2 = torch.empty_like(lse).view(rows, w.num_heads)
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(g2, stream=stream):
-                for _ in range(K):
-                    B.combine(part_out, part_lse, out2, lse2)
-        g2.replay()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            g2.replay()
-            c1.record(stream)
-        torch.cuda.synchronize()
-        combine_us = c0.elapsed_time(c1) * 1e3 / K
-    partial_us = max(call_us - combine_us, 1e-3)
+        part_out, part_lse = B.workspace_parts(plan, ws)
+        out2 = torch.empty_like(out).view(plan.rows, w.num_heads, w.d_v)
+        lse2 = torch.empty_like(lse).view(plan.rows, w.num_heads)
+        combine_us = time_graph(capture(lambda i: B.combine(part_out, part_lse, out2, lse2)))
 
     gbs = gathered / (call_us * 1e-6) / 1e9
     kernel_gbs = gathered / (partial_us * 1e-6) / 1e9

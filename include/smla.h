@@ -133,6 +133,25 @@ smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The first half of smla_decode_run: the partial-attention kernel alone, with
+ * the same arguments and checks.  With plan->num_splits == 1 it writes the
+ * final out and lse (the whole decode).  Otherwise it leaves the per-part
+ * results in the workspace, for smla_combine (or an exchange between devices
+ * first: parts computed on different devices over disjoint index lists merge
+ * the same way; "The Moment of Truth: Analyzing a Custom MMA Kernel's
+ * Performance on Blackwell GPUs", "The Split-K Solution: Reasoning About the
+ * Fix"), laid out as
+ *   part_out = (float *)workspace                   fp32 [S, R, H, d_v]
+ *   part_lse = part_out + S * R * H * d_v           fp32 [S, R, H]
+ * with S = plan->num_splits; out and lse are then not written.  An empty
+ * part has part_lse = -inf and part_out = 0.
+ */
+smla_status_t smla_decode_partial(const smla_plan_t *plan, const void *q, const void *kv_cache,
+                                  int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,
+                                  const int32_t *seq_lens, float softmax_scale, void *out, float *lse,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Log-sum-exp merge of partial attention results over disjoint parts of a
  * list ("The Moment of Truth: Analyzing a Custom MMA Kernel's Performance
  * on Blackwell GPUs", "The Split-K Solution: Reasoning About the Fix").
@@ -140,8 +159,11 @@ smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void
  *   part_lse  fp32 [num_splits, rows, num_heads]: per-part lse, -inf for an empty part
  *   out       bf16 [rows, num_heads, d_v];  lse fp32 [rows, num_heads]
  * out = sum_i exp(lse_i - lse) * part_out_i with lse = ln sum_i exp(lse_i);
- * parts with lse_i = -inf carry no weight; if every part is empty,
- * out = 0 and lse = -inf.  Supported: d_v a multiple of 4, num_splits >= 1.
+ * parts with lse_i = -inf carry no weight and their part_out values are
+ * ignored (even NaN); if every part is empty, out = 0 and lse = -inf.
+ * Supported: d_v = 512 (else SMLA_ERR_UNSUPPORTED), num_splits >= 1,
+ * rows * num_heads < 2^31; part_out and out 16-byte aligned (else
+ * SMLA_ERR_INVALID_ARG).  Asynchronous on `stream`; allocates nothing.
  */
 smla_status_t smla_combine(const float *part_out, const float *part_lse, int32_t num_splits, int32_t rows,
                            int32_t num_heads, int32_t d_v, void *out, float *lse, void *stream);

@@ -69,6 +69,8 @@ def load(path: Optional[str] = None):
     lib.smla_decode_run.argtypes = [ctypes.POINTER(Plan), P, P, ctypes.c_int64, P, P, P, ctypes.c_float,
                                     P, P, P, ctypes.c_size_t, P]
     lib.smla_decode_run.restype = ctypes.c_int
+    lib.smla_decode_partial.argtypes = lib.smla_decode_run.argtypes
+    lib.smla_decode_partial.restype = ctypes.c_int
     lib.smla_combine.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.smla_combine.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +122,26 @@ def decode_run(plan: Plan, q, kv_cache, block_table, indices, seq_lens, softmax_
                                   _ptr(indices), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse),
                                   _ptr(workspace), ws_bytes, _stream(stream)),
            "smla_decode_run")
+
+
+def decode_partial(plan: Plan, q, kv_cache, block_table, indices, seq_lens, softmax_scale: float, out, lse,
+                   workspace=None, stream=None) -> None:
+    """Enqueue smla_decode_partial (the partial-attention kernel alone)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    num_blocks = kv_cache.shape[0] if kv_cache is not None else 0
+    _check(load().smla_decode_partial(ctypes.byref(plan), _ptr(q), _ptr(kv_cache), num_blocks, _ptr(block_table),
+                                      _ptr(indices), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse),
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "smla_decode_partial")
+
+
+def workspace_parts(plan: Plan, workspace):
+    """Views (part_out [S, rows, H, d_v], part_lse [S, rows, H]) of a split plan's workspace."""
+    import torch
+    S, rows, H, dv = plan.num_splits, plan.rows, plan.prob.num_heads, plan.prob.d_v
+    n_out = S * rows * H * dv
+    f = workspace.view(torch.float32)
+    return f[:n_out].view(S, rows, H, dv), f[n_out:n_out + S * rows * H].view(S, rows, H)
 
 
 def combine(part_out, part_lse, out, lse, stream=None) -> None:

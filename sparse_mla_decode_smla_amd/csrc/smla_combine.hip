@@ -4,13 +4,19 @@
 // results over chunks of the top-k list are reduced by a separate combine
 // kernel).
 //
-// For each (row, head) pair and each 4-wide slice of the value dims:
+// For each (row, head) pair:
 //   M = max_i lse_i;  lse = M + ln sum_i exp(lse_i - M);
-//   out = sum_i exp(lse_i - lse) * part_out_i  (parts with lse_i = -inf skipped),
+//   out = sum_i exp(lse_i - lse) * part_out_i  (parts with lse_i = -inf are
+//   ignored, whatever their part_out holds),
 // accumulated in fp32 and rounded to bf16 at the store.  A pair whose parts
-// are all empty gets out = 0 and lse = -inf.  Memory bound: every partial
-// byte is read once with 16-byte loads, consecutive threads on consecutive
-// slices of the same pair.
+// are all empty gets out = 0 and lse = -inf.
+//
+// One wave per pair.  The weights of all parts are computed once, lane i
+// holding part i (then i + 64, ...), with wave-wide max / sum reductions;
+// the output loop then streams the parts' rows with 16-byte loads, lane l
+// owning 8 consecutive value dims, in batches of kBatch parts whose loads are
+// all issued before any is consumed, so a pair costs about S / kBatch memory
+// round trips rather than S.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -22,57 +28,98 @@ namespace smla {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kCombineThreads = 256;
+constexpr int kBatch = 16;  // parts whose loads are in flight together
+static_assert(64 % kBatch == 0, "a batch never straddles two 64-part chunks");
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_out,
-                                                                  const float* __restrict__ part_lse,
-                                                                  int num_splits, int64_t pairs, int d_v,
-                                                                  uint16_t* __restrict__ out,
-                                                                  float* __restrict__ lse) {
-    const int slices = d_v / 4;
-    const int64_t items = pairs * slices;
-    for (int64_t it = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x; it < items;
-         it += (int64_t)gridDim.x * kCombineThreads) {
-        const int64_t pair = it / slices;
-        const int c = (int)(it - pair * slices);
-        float M = -INFINITY;
-        for (int s = 0; s < num_splits; ++s) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        float total = -INFINITY;
-        if (M != -INFINITY) {
-            float z = 0.f;
-            for (int s = 0; s < num_splits; ++s) {
-                const float l = part_lse[(int64_t)s * pairs + pair];
-                if (l != -INFINITY) z += expf(l - M);
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// d_v == 512: lane l owns dims [8l, 8l + 8).  Grid: one 64-thread workgroup per pair.
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_out,
+                                                     const float* __restrict__ part_lse, int num_splits,
+                                                     int64_t pairs, uint16_t* __restrict__ out,
+                                                     float* __restrict__ lse) {
+    const int64_t pair = blockIdx.x;
+    const int lane = threadIdx.x;
+
+    // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...)
+    float M = -INFINITY;
+    for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
+    M = wave_max(M);
+    float total = -INFINITY;
+    if (M != -INFINITY) {
+        float z = 0.f;
+        for (int s = lane; s < num_splits; s += 64) {
+            const float l = part_lse[(int64_t)s * pairs + pair];
+            z += l == -INFINITY ? 0.f : expf(l - M);
+        }
+        total = M + logf(wave_sum(z));
+    }
+
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    if (total != -INFINITY) {
+        const float* base = part_out + pair * kDv + 8 * lane;
+        const int64_t part_stride = pairs * kDv;
+        for (int s0 = 0; s0 < num_splits; s0 += 64) {
+            // weight of part s0 + lane (0 for an empty part or past the end)
+            float w = 0.f;
+            if (s0 + lane < num_splits) {
+                const float l = part_lse[(int64_t)(s0 + lane) * pairs + pair];
+                w = l == -INFINITY ? 0.f : expf(l - total);
             }
-            total = M + logf(z);
-            for (int s = 0; s < num_splits; ++s) {
-                const float l = part_lse[(int64_t)s * pairs + pair];
-                if (l == -INFINITY) continue;
-                const f32x4 v = *(const f32x4*)(part_out + ((int64_t)s * pairs + pair) * d_v + 4 * c);
-                acc += expf(l - total) * v;
+            const int n = min(64, num_splits - s0);
+            for (int j0 = 0; j0 < n; j0 += kBatch) {
+                f32x4 v0[kBatch], v1[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    // parts past the end re-read the last part (in bounds) with weight 0
+                    const int s = s0 + min(j0 + j, n - 1);
+                    const float* p = base + (int64_t)s * part_stride;
+                    v0[j] = *(const f32x4*)p;
+                    v1[j] = *(const f32x4*)(p + 4);
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float wj = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j0 + j, 63)));
+                    // (past the end wj is 0.)  A select, not a branch, so the loads
+                    // stay batched; an ignored part adds nothing, not even a NaN.
+                    const bool use = wj != 0.f;
+                    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc0 += wj * (use ? v0[j] : zero);
+                    acc1 += wj * (use ? v1[j] : zero);
+                }
             }
         }
-        bf16x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = (__bf16)acc[j];
-        *(bf16x4*)(out + pair * d_v + 4 * c) = o;
-        if (c == 0) lse[pair] = total;
     }
+    bf16x8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[j] = (__bf16)acc0[j];
+        o[4 + j] = (__bf16)acc1[j];
+    }
+    *(bf16x8*)(out + pair * kDv + 8 * lane) = o;
+    if (lane == 0) lse[pair] = total;
 }
 
 }  // namespace
 
 smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
-                             int d_v, void* out, float* lse, hipStream_t stream) {
-    const int64_t items = pairs * (d_v / 4);
-    if (items == 0) return SMLA_OK;
-    int64_t blocks = (items + kCombineThreads - 1) / kCombineThreads;
-    if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, stream, part_out,
-                       part_lse, num_splits, pairs, d_v, (uint16_t*)out, lse);
+                             void* out, float* lse, hipStream_t stream) {
+    if (pairs == 0) return SMLA_OK;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)pairs), dim3(64), 0, stream, part_out, part_lse, num_splits,
+                       pairs, (uint16_t*)out, lse);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -82,11 +129,12 @@ extern "C" smla_status_t smla_combine(const float* part_out, const float* part_l
                                       int32_t rows, int32_t num_heads, int32_t d_v, void* out, float* lse,
                                       void* stream) {
     if (num_splits < 1 || rows < 0 || num_heads < 0 || d_v <= 0) return SMLA_ERR_INVALID_ARG;
-    if (d_v % 4 != 0) return SMLA_ERR_UNSUPPORTED;
+    if (d_v != smla::kDv) return SMLA_ERR_UNSUPPORTED;
     const int64_t pairs = (int64_t)rows * num_heads;
     if (pairs == 0) return SMLA_OK;
+    if (pairs > 0x7fffffffLL) return SMLA_ERR_UNSUPPORTED;
     if (!part_out || !part_lse || !out || !lse) return SMLA_ERR_INVALID_ARG;
-    if (((uintptr_t)part_out & 15) != 0 || ((uintptr_t)out & 7) != 0) return SMLA_ERR_INVALID_ARG;
+    if (((uintptr_t)part_out & 15) != 0 || ((uintptr_t)out & 15) != 0) return SMLA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return smla::launch_combine(part_out, part_lse, num_splits, pairs, d_v, out, lse, (hipStream_t)stream);
+    return smla::launch_combine(part_out, part_lse, num_splits, pairs, out, lse, (hipStream_t)stream);
 }

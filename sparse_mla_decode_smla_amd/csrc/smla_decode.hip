@@ -39,7 +39,7 @@
 namespace smla {
 
 smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
-                             int d_v, void* out, float* lse, hipStream_t stream);
+                             void* out, float* lse, hipStream_t stream);
 
 namespace {
 
@@ -544,25 +544,53 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             a.part_lse[((int64_t)sp * a.rows + r) * kHeads + h] = lse_v;
     }
     __syncthreads();
+    // The normalised output goes through the (now idle) stage ring, 32 heads at
+    // a time, so that every head's row is written to HBM with contiguous
+    // 1 KB stores instead of 64-byte pieces of 16 rows per instruction.  Rows
+    // are padded by 16 bytes: the staging writes of a 16-lane group (16 heads,
+    // same dims) then fall on distinct banks.  (Every stage DMA has landed:
+    // the last loop iteration waited for all of them.)
+    constexpr int kRowPitch = 4 * kDv + 16;
+    static_assert(32 * kRowPitch <= NST * STAGE, "staging area exceeds the stage ring");
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-        const int h = 16 * hb + i16;
-        const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h);
-        const float inv = lt == 0.f ? 0.f : 1.f / lt;
-        if (a.num_splits == 1) {
-            uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 128 * wave + 4 * g;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                bf16x4 v;
+        for (int hl = 0; hl < 2; ++hl) {
+            const int hb = 2 * half + hl;
+            const int h = 16 * hb + i16;
+            const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h);
+            const float inv = lt == 0.f ? 0.f : 1.f / lt;
+            lds_u8* row = lds + (h - 32 * half) * kRowPitch + 4 * (128 * wave + 4 * g);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = (__bf16)(oacc[db][hb][j] * inv);
-                *(bf16x4*)(o + 16 * db) = v;
-            }
-        } else {
-            float* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 128 * wave + 4 * g;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = oacc[db][hb] * inv;
+            for (int db = 0; db < 8; ++db)
+                *(__attribute__((address_space(3))) f32x4*)(row + 64 * db) = oacc[db][hb] * inv;
         }
+        __syncthreads();
+        // wave w stores heads 32*half + 8w .. 32*half + 8w + 7; lane l holds dims
+        // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int hl = 8 * wave + j;
+            const int h = 32 * half + hl;
+            const f32x4 x0 = lds_load<f32x4>(lds + hl * kRowPitch + 16 * lane);
+            const f32x4 x1 = lds_load<f32x4>(lds + hl * kRowPitch + 1024 + 16 * lane);
+            if (a.num_splits == 1) {
+                uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 4 * lane;
+                bf16x4 v0, v1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v0[e] = (__bf16)x0[e];
+                    v1[e] = (__bf16)x1[e];
+                }
+                *(bf16x4*)o = v0;
+                *(bf16x4*)(o + 256) = v1;
+            } else {
+                float* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 4 * lane;
+                *(f32x4*)o = x0;
+                *(f32x4*)(o + 256) = x1;
+            }
+        }
+        if (half == 0) __syncthreads();  // the staging rows are free again
     }
 }
 
@@ -589,12 +617,16 @@ hipError_t launch_partial(const PartialArgs& args, int grid, size_t lds_bytes, h
 }  // namespace
 }  // namespace smla
 
-extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q, const void* kv_cache,
-                                         int64_t num_kv_blocks, const int32_t* block_table,
-                                         const int32_t* indices, const int32_t* seq_lens, float softmax_scale,
-                                         void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                         void* stream) {
-    using namespace smla;
+namespace smla {
+namespace {
+
+// Host checks shared by smla_decode_partial and smla_decode_run; on success
+// the partial kernel is enqueued (which, with one part, writes the final
+// result).
+smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void* kv_cache, int64_t num_kv_blocks,
+                              const int32_t* block_table, const int32_t* indices, const int32_t* seq_lens,
+                              float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, PartialArgs* args_out) {
     if (!plan) return SMLA_ERR_INVALID_ARG;
     // The plan must be exactly what smla_decode_plan gives for its problem.
     smla_plan_t check;
@@ -613,7 +645,7 @@ extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q,
         if (((uintptr_t)workspace & 255) != 0) return SMLA_ERR_INVALID_ARG;
     }
 
-    PartialArgs args;
+    PartialArgs& args = *args_out;
     args.q = (const uint16_t*)q;
     args.kv = (const uint8_t*)kv_cache;
     args.block_table = block_table;
@@ -634,12 +666,37 @@ extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q,
     args.num_splits = S;
     args.scale_log2 = softmax_scale * kLog2e;
 
-    hipStream_t s = (hipStream_t)stream;
     const size_t lds = partial_lds_bytes(plan->prob.kv_format, plan->tokens_per_split);
     (void)hipGetLastError();  // clear an earlier, unrelated error
-    hipError_t e = plan->prob.kv_format == SMLA_KV_BF16 ? launch_partial<0>(args, plan->num_workgroups, lds, s)
-                                                        : launch_partial<1>(args, plan->num_workgroups, lds, s);
-    if (e != hipSuccess) return SMLA_ERR_LAUNCH;
-    if (S > 1) return launch_combine(args.part_out, args.part_lse, S, pairs, kDv, out, lse, s);
-    return SMLA_OK;
+    hipError_t e = plan->prob.kv_format == SMLA_KV_BF16 ? launch_partial<0>(args, plan->num_workgroups, lds, stream)
+                                                        : launch_partial<1>(args, plan->num_workgroups, lds, stream);
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace smla
+
+extern "C" smla_status_t smla_decode_partial(const smla_plan_t* plan, const void* q, const void* kv_cache,
+                                             int64_t num_kv_blocks, const int32_t* block_table,
+                                             const int32_t* indices, const int32_t* seq_lens, float softmax_scale,
+                                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+    smla::PartialArgs args;
+    return smla::enqueue_partial(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens, softmax_scale,
+                                 out, lse, workspace, workspace_bytes, (hipStream_t)stream, &args);
+}
+
+extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q, const void* kv_cache,
+                                         int64_t num_kv_blocks, const int32_t* block_table,
+                                         const int32_t* indices, const int32_t* seq_lens, float softmax_scale,
+                                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    using namespace smla;
+    PartialArgs args;
+    smla_status_t st = enqueue_partial(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens,
+                                       softmax_scale, out, lse, workspace, workspace_bytes, (hipStream_t)stream,
+                                       &args);
+    if (st != SMLA_OK || plan->rows == 0 || plan->num_splits == 1) return st;
+    return launch_combine(args.part_out, args.part_lse, plan->num_splits, (int64_t)plan->rows * kHeads, out, lse,
+                          (hipStream_t)stream);
 }

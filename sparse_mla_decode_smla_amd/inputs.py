@@ -111,11 +111,13 @@ class Inputs:
     def num_kv_blocks(self) -> int:
         return int(self.kv_cache.shape[0])
 
-    def valid_count(self, indices: Optional[np.ndarray] = None) -> int:
-        """Number of index entries that select a token (the gathered-token count)."""
+    def valid_count(self, indices: Optional[np.ndarray] = None, seq_lens: Optional[np.ndarray] = None) -> int:
+        """Number of index entries that select a token (the gathered-token count).
+
+        `indices` [b, q_len, topk] and `seq_lens` [b] may be a subset of the sequences."""
         idx = self.indices if indices is None else indices
-        cap = np.minimum(self.seq_lens.astype(np.int64),
-                         self.workload.block_size * self.block_table.shape[1])
+        sl = self.seq_lens if seq_lens is None else seq_lens
+        cap = np.minimum(sl.astype(np.int64), self.workload.block_size * self.block_table.shape[1])
         return int(((idx >= 0) & (idx < cap[:, None, None])).sum())
 
 

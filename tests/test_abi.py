@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"smla_decode_plan", "smla_decode_run", "smla_combine", "smla_status_string"}
+    assert set(names) >= {"smla_decode_plan", "smla_decode_run", "smla_decode_partial", "smla_combine",
+                          "smla_status_string"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in smla.h but not exported"
@@ -101,17 +102,22 @@ def test_plan_rejects(kw, status):
     assert e.value.status == status
 
 
+ENTRY = "smla_decode_run"
+
+
 def _run(plan, **kw):
     lib = B.load()
     args = dict(q=1 << 20, kv=1 << 21, nb=16, bt=1 << 22, idx=1 << 23, sl=None, scale=0.04, out=1 << 24,
                 lse=1 << 25, ws=None, wsb=0)
     args.update(kw)
-    return lib.smla_decode_run(ctypes.byref(plan) if plan is not None else None, args["q"], args["kv"], args["nb"],
+    return getattr(lib, ENTRY)(ctypes.byref(plan) if plan is not None else None, args["q"], args["kv"], args["nb"],
                                args["bt"], args["idx"], args["sl"], args["scale"], args["out"], args["lse"],
                                args["ws"], args["wsb"], None)
 
 
-def test_run_argument_checks_need_no_gpu():
+@pytest.mark.parametrize("entry", ["smla_decode_run", "smla_decode_partial"])
+def test_run_argument_checks_need_no_gpu(entry, monkeypatch):
+    monkeypatch.setitem(globals(), "ENTRY", entry)
     plan = B.decode_plan(2, 1, 256, 8, num_cus=256)
     assert plan.workspace_bytes > 0
     assert _run(None) == 1
@@ -135,3 +141,5 @@ def test_combine_argument_checks_need_no_gpu():
     assert lib.smla_combine(1 << 20, 1 << 21, 2, 1, 64, 510, 1 << 22, 1 << 23, None) == 2
     assert lib.smla_combine(None, None, 2, 0, 64, 512, None, None, None) == 0
     assert lib.smla_combine(None, 1 << 21, 2, 1, 64, 512, 1 << 22, 1 << 23, None) == 1
+    assert lib.smla_combine((1 << 20) + 8, 1 << 21, 2, 1, 64, 512, 1 << 22, 1 << 23, None) == 1  # misaligned
+    assert lib.smla_combine(1 << 20, 1 << 21, 2, 1, 64, 512, (1 << 22) + 8, 1 << 23, None) == 1

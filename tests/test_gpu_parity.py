@@ -183,14 +183,17 @@ def test_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_combine_kernel_alone():
-    rng = np.random.default_rng(70)
-    S, rows, H, dv = 5, 3, 64, 512
+@pytest.mark.parametrize("S", [1, 5, 70])
+def test_combine_kernel_alone(S):
+    rng = np.random.default_rng(70 + S)
+    rows, H, dv = 3, 64, 512
     po = rng.standard_normal((S, rows, H, dv)).astype(np.float32)
     pl = (rng.standard_normal((S, rows, H)) * 3).astype(np.float32)
-    pl[1, 0, :] = -np.inf
+    if S > 1:
+        pl[1, 0, :] = -np.inf
+        po[1, 0, :, :] = np.nan                 # an empty part's values are ignored
     pl[:, 2, 5] = -np.inf                       # every part of one pair empty
-    ref_o, ref_l = oracle.lse_combine(po.astype(np.float64), pl.astype(np.float64))
+    ref_o, ref_l = oracle.lse_combine(np.nan_to_num(po).astype(np.float64), pl.astype(np.float64))
     out = torch.empty((rows, H, dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((rows, H), dtype=torch.float32, device="cuda")
     B().combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, lse)
@@ -201,6 +204,29 @@ def test_combine_kernel_alone():
     assert np.all(o[~fin] == 0) and np.all(np.isneginf(lg[~fin]))
     assert np.abs(o[fin] - ref_o[fin]).max() <= 2 ** -8 * np.abs(ref_o[fin]).max() + 1e-6
     assert np.abs(lg[fin] - ref_l[fin]).max() <= 1e-5 * max(1.0, np.abs(ref_l[fin]).max())
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_partial_then_combine_equals_run(splits):
+    """smla_decode_partial + smla_combine is smla_decode_run, bit for bit."""
+    inp = I.small_inputs(batch=2, q_len=1, topk=300, seq_len=900, kv_format=I.KV_BF16, seed=81)
+    w = inp.workload
+    q, kv, bt, idx, sl = B().to_device(inp)
+    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, force_splits=splits)
+    out_a = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device="cuda")
+    lse_a = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device="cuda")
+    out_b, lse_b = torch.empty_like(out_a), torch.empty_like(lse_a)
+    ws = B().alloc_workspace(plan, "cuda")
+    B().decode_run(plan, q, kv, bt, idx, sl, inp.softmax_scale, out_a, lse_a, ws)
+    torch.cuda.synchronize()
+    ws2 = B().alloc_workspace(plan, "cuda")
+    B().decode_partial(plan, q, kv, bt, idx, sl, inp.softmax_scale, out_b, lse_b, ws2)
+    if plan.num_splits > 1:
+        po, pl = B().workspace_parts(plan, ws2)
+        B().combine(po, pl, out_b.view(plan.rows, w.num_heads, w.d_v), lse_b.view(plan.rows, w.num_heads))
+    torch.cuda.synchronize()
+    assert plan.num_splits == splits
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
 
 
 def test_runs_on_a_side_stream():
