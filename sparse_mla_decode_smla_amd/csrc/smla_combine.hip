@@ -14,9 +14,9 @@
 // One wave per pair.  The weights of all parts are computed once, lane i
 // holding part i (then i + 64, ...), with wave-wide max / sum reductions;
 // the output loop then streams the parts' rows with 16-byte loads, lane l
-// owning 8 consecutive value dims, in batches of kBatch parts whose loads are
-// all issued before any is consumed, so a pair costs about S / kBatch memory
-// round trips rather than S.
+// owning 8 consecutive value dims, in batches of 16, 8, 4 or 1 parts (fitting
+// S exactly) whose loads are all issued before any is consumed, so a pair
+// costs about S / 16 memory round trips rather than S.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,9 +30,6 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBatch = 16;  // parts whose loads are in flight together
-static_assert(64 % kBatch == 0, "a batch never straddles two 64-part chunks");
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -43,6 +40,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
+}
+
+// Adds parts s_first .. s_first + NB - 1 (weights in lanes w_lane .. w_lane + NB - 1
+// of `w`) to the accumulators; all 2 * NB loads are issued before any is used.
+template <int NB>
+__device__ __forceinline__ void add_parts(const float* base, int64_t part_stride, int s_first, int w_lane, float w,
+                                          f32x4& acc0, f32x4& acc1) {
+    f32x4 v0[NB], v1[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const float* p = base + (int64_t)(s_first + j) * part_stride;
+        v0[j] = *(const f32x4*)p;
+        v1[j] = *(const f32x4*)(p + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), w_lane + j));
+        // a select, not a branch, so the loads stay batched; an ignored part
+        // (weight 0) adds nothing, not even a NaN
+        const bool use = wj != 0.f;
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc0 += wj * (use ? v0[j] : zero);
+        acc1 += wj * (use ? v1[j] : zero);
+    }
 }
 
 // d_v == 512: lane l owns dims [8l, 8l + 8).  Grid: one 64-thread workgroup per pair.
@@ -79,28 +100,11 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
                 w = l == -INFINITY ? 0.f : expf(l - total);
             }
             const int n = min(64, num_splits - s0);
-            for (int j0 = 0; j0 < n; j0 += kBatch) {
-                f32x4 v0[kBatch], v1[kBatch];
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    // parts past the end re-read the last part (in bounds) with weight 0
-                    const int s = s0 + min(j0 + j, n - 1);
-                    const float* p = base + (int64_t)s * part_stride;
-                    v0[j] = *(const f32x4*)p;
-                    v1[j] = *(const f32x4*)(p + 4);
-                }
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const float wj = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j0 + j, 63)));
-                    // (past the end wj is 0.)  A select, not a branch, so the loads
-                    // stay batched; an ignored part adds nothing, not even a NaN.
-                    const bool use = wj != 0.f;
-                    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-                    acc0 += wj * (use ? v0[j] : zero);
-                    acc1 += wj * (use ? v1[j] : zero);
-                }
-            }
+            int j0 = 0;
+            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, w, acc0, acc1);
+            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, w, acc0, acc1); j0 += 8; }
+            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, w, acc0, acc1); j0 += 4; }
+            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, w, acc0, acc1);
         }
     }
     bf16x8 o;

@@ -14,9 +14,11 @@ constexpr int kDv = 512;         // value width = c_kv part
 constexpr int kDr = kDqk - kDv;  // rope width
 constexpr int kBlock = 64;       // tokens per cache block
 
-// Workgroup shape of the partial-attention kernel: 4 waves of 64 lanes; wave w
-// owns heads [16w, 16w + 16) for both contractions.
-constexpr int kWaves = 4;
+// Workgroup shape of the partial-attention kernel: 8 waves of 64 lanes, two
+// per SIMD.  For QK^T wave w owns heads [16(w%4), 16(w%4) + 16) and tokens
+// [16(w/4), 16(w/4) + 16) of a tile; for PV it owns value dims
+// [64w, 64w + 64) of all 64 heads.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;        // tokens gathered per pipeline stage
 
@@ -37,15 +39,20 @@ constexpr int kStageBytesFp8 = kBandsFp8 * kTile * 128 + kTile * 16;
 constexpr int kStagesBf16 = 4;
 constexpr int kStagesFp8 = 6;
 
-// Exchange area after the stage ring: the softmax weights P of each wave's
-// 16 heads in MFMA operand order (64 lanes x 16 B per wave; for fp8 rows one
-// copy per 128-group with that group's per-token scale folded in), the
-// per-wave restart flags and the per-head softmax denominators.
-constexpr int kPBytesPerCopy = kWaves * 64 * 16;
+// Exchange area after the stage ring:
+//   P      the softmax weights of a tile, bf16, in the order of the PV
+//          B operand: [16-head block][4 lane groups][16 heads] x 16 bytes
+//          (8 bytes from each token half); for fp8 rows one copy per
+//          128-group with that group's per-token scale folded in;
+//   flags  one restart flag per wave;
+//   tmax   per-head maxima of the two token halves [2][64] fp32;
+//   denom  per-head softmax denominators of the two token halves [2][64] fp32.
+constexpr int kPBytesPerCopy = kHeads * kTile * 2;
 inline constexpr int aux_p_bytes(int kv_format) { return kv_format == 0 ? kPBytesPerCopy : 4 * kPBytesPerCopy; }
 inline constexpr int aux_flag_offset(int kv_format) { return aux_p_bytes(kv_format); }
-inline constexpr int aux_denom_offset(int kv_format) { return aux_p_bytes(kv_format) + 64; }
-inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + kHeads * 4; }
+inline constexpr int aux_tmax_offset(int kv_format) { return aux_flag_offset(kv_format) + 64; }
+inline constexpr int aux_denom_offset(int kv_format) { return aux_tmax_offset(kv_format) + 2 * kHeads * 4; }
+inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + 2 * kHeads * 4; }
 
 constexpr int kLdsLimit = 160 * 1024;  // bytes of LDS a gfx950 workgroup may use
 
