@@ -31,6 +31,9 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms stay disabled in the GPU code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in VGPRs: the partial kernel keeps Q in AGPRs and its
+           # output accumulators in VGPRs, which fits two waves per SIMD unspilled
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wall", "-Wno-unused-command-line-argument"]
     for inc in INCLUDE:
         cmd += ["-I", inc]

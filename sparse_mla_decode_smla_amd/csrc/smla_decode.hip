@@ -75,13 +75,15 @@ struct PartialArgs {
 };
 
 // 16-byte LDS-DMA load: lane l's 16 bytes from `src` land at LDS byte
-// lds_base + 16*l.  Issued from inline assembly so the compiler does not
+// lds_base + 16*l (lds_base is the same in every lane).  Issued from inline assembly so the compiler does not
 // serialise the stage ring with conservative waits; the kernel waits on
 // vmcnt itself.  M0 is written only here (the kernel has no other M0 use).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -137,13 +139,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int NST = FMT == 0 ? kStagesBf16 : kStagesFp8;
     constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : kRowBytesFp8;
     constexpr int NBANDS = FMT == 0 ? kBandsBf16 : kBandsFp8;
-    static_assert(NST - 2 <= 4, "wait_tiles covers at most 4 tiles in flight after the current one");
+    constexpr int LPT = NBANDS + (FMT == 0 ? 0 : 1);  // DMA instructions per PV wave per tile
+    constexpr int PBUF = aux_p_buffer_bytes(FMT);
+    static_assert(NST >= 3 && NST - 3 <= 4, "stage ring depth outside what the waits cover");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_generic[];
     lds_u8* lds = (lds_u8*)smem_generic;
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
+    constexpr int AUX_ALPHA = aux_alpha_offset(FMT);
     constexpr int AUX_FLAG = aux_flag_offset(FMT);
-    constexpr int AUX_TMAX = aux_tmax_offset(FMT);
     constexpr int AUX_DENOM = aux_denom_offset(FMT);
     lds_u8* aux = lds + NST * STAGE;
     lds_u8* rowtab = aux + aux_bytes(FMT);  // int32 per token of this part: physical row or -1
@@ -151,11 +155,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hg = wave & 3;    // QK head group: heads [16hg, 16hg + 16)
-    const int tb = wave >> 2;   // QK token half of a tile: tokens [16tb, 16tb + 16)
     const int g = lane >> 4;    // 16-lane group
     const int i16 = lane & 15;  // lane within the group
-    const int head = 16 * hg + i16;  // the head of this lane in QK and softmax
 
     const int r = blockIdx.x / a.num_splits;
     const int sp = blockIdx.x - r * a.num_splits;
@@ -164,25 +165,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
     const int ntiles = (nk + kTile - 1) / kTile;
 
-    // ---- Q of head 16hg + i16, as the B operand of S^T = K . Q^T (8 dims of
-    // k-step kk per lane).  For fp8 rows the c_kv dims of k-steps 2p and 2p+1
-    // inside a 128-group are the two halves of one 16-byte run, so one LDS
-    // read feeds two k-steps.
-    bf16x8 qreg[18];
-    {
-        const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * kDqk;
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-            int d;
-            if (FMT == 0 || kk >= 16)
-                d = 32 * kk + 8 * g;
-            else
-                d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
-            qreg[kk] = *(const bf16x8*)(qh + d);
-        }
-    }
-
-    // ---- logical positions -> physical rows (masked entries -> -1)
+    // ---- logical positions -> physical rows (masked entries -> -1), all waves
     {
         int64_t cap = (int64_t)kBlock * a.max_blocks;
         if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
@@ -200,345 +183,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
         }
     }
-    wait_vmcnt<0>();
-    // The loads above are complete; tell the compiler so it does not place
-    // vmcnt waits for them inside the loop, where the stage DMAs are in flight.
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qreg[kk]));
-    __syncthreads();
 
-    // ---- gather: a DMA instruction moves one 128-byte band of 8 tokens.  Wave
-    // w takes the tokens [8(w%4), 8(w%4) + 8) of every tile and the bands
-    //   bf16: w/4, w/4 + 2, w/4 + 4, w/4 + 6, and band 8 if w < 4  (5 or 4 DMAs)
-    //   fp8 : 0, 2, 4 if w < 4; 1, 3 and the fp32 scales otherwise (3 DMAs)
-    // so each wave issues a fixed number of DMAs per tile and counts them itself.
-    constexpr int LPT_A = FMT == 0 ? 5 : 3;  // DMAs per tile of waves 0-3
-    constexpr int LPT_B = FMT == 0 ? 4 : 3;  // DMAs per tile of waves 4-7
-    auto issue = [&](int tile) {
-        const unsigned sbase = lds0 + (unsigned)((tile % NST) * STAGE);
-        const int t = 8 * hg + (lane >> 3);  // token of this lane within the tile
-        const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
-        const int chunk = (lane & 7) ^ swz(t);
-        const unsigned char* src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
-        const int bstride = row >= 0 ? 128 : 0;
-        const unsigned dst = sbase + (unsigned)(8 * hg * 128);
-        if (FMT == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int bd = tb + 2 * i;
-                lds_dma16(src + bd * bstride, dst + (unsigned)(bd * kTile * 128));
-            }
-            if (tb == 0) lds_dma16(src + 8 * bstride, dst + (unsigned)(8 * kTile * 128));
-        } else {
-            if (tb == 0) {
-#pragma unroll
-                for (int bd = 0; bd < 5; bd += 2) lds_dma16(src + bd * bstride, dst + (unsigned)(bd * kTile * 128));
-            } else {
-#pragma unroll
-                for (int bd = 1; bd < 4; bd += 2) lds_dma16(src + bd * bstride, dst + (unsigned)(bd * kTile * 128));
-                // fp32 scales: lanes 0..7 fetch the 16 bytes of tokens 8hg + lane
-                const int t2 = 8 * hg + (lane & 7);
-                const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
-                const unsigned char* s2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
-                if (lane < 8) lds_dma16(s2, sbase + (unsigned)(NBANDS * kTile * 128 + 8 * hg * 16));
-            }
-        }
-    };
-    auto wait_for_tile = [&](int after) {
-        if (wave < 4)
-            wait_tiles<LPT_A>(after);
-        else
-            wait_tiles<LPT_B>(after);
-    };
-
-    // ---- per-lane LDS byte offsets inside a stage (loop invariant)
-    // QK A operand (K): token tA = 16tb + i16, chunk (4e + g) of a band (e = k-step parity).
-    const int tA = 16 * tb + i16;
-    int qk[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) qk[e] = tA * 128 + (((4 * e + g) ^ swz(tA)) << 4);
-    // QK accumulator entry j of this lane: token tC + j of the tile (tC = 16tb + 4g).
-    const int tC = 16 * tb + 4 * g;
-    // PV A operand (V^T) of dims [64w, 64w + 64): the k-slots 8g .. 8g + 7 of a
-    // lane are the tokens 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 (the order in
-    // which the P operand is exchanged).
-    //   bf16: band w; lane i16 addresses token tok + (i16 >> 2), 4 dims at 4(i16 & 3)
-    //         of 16-dim block m; the transpose read hands lane i dim i of the block.
-    //   fp8 : band w/2 (the scale group), 16-dim blocks 4(w & 1) + m; lane i16
-    //         addresses token slot j = i16 >> 1, 8 dims at 8(i16 & 1).
-    int pv[8];
-    if (FMT == 0) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int ta = 16 * blk + 4 * g + (i16 >> 2);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                pv[4 * blk + m] = (wave * kTile + ta) * 128 + (((2 * m + ((i16 & 3) >> 1)) ^ swz(ta)) << 4) +
-                                  8 * (i16 & 1);
-        }
-    } else {
-        const int j = i16 >> 1;
-        const int ta = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            pv[m] = ((wave >> 1) * kTile + ta) * 128 + (((4 * (wave & 1) + m) ^ swz(ta)) << 4) + 8 * (i16 & 1);
-    }
-    // P: this lane's 4 weights (tokens tC .. tC + 3 of head `head`) go to
-    // operand slot (block hg, group g, lane i16), half tb.
-    lds_u8* const p_mine = aux + ((hg * 4 + g) * 16 + i16) * 16 + 8 * tb;  // + grp * kPBytesPerCopy for fp8
-    const lds_u8* const p_read = aux + (FMT == 0 ? 0 : (wave >> 1) * kPBytesPerCopy) + lane * 16;  // + hb * 1024
-
-    // Softmax state of head `head` over this wave's token half.  Exponentials
-    // are taken against a reference fixed at the first tile with a valid token
-    // (the max over that tile, both halves), so the accumulators are never
-    // rescaled inside the loop; weights up to 2^kMaxRise stay finite in fp32
-    // and bf16.  If a later score rises above the reference by more than that,
-    // the workgroup restarts its part of the list with the reference raised
-    // (the row table and Q stay; the accumulators of the abandoned pass are
-    // discarded).
-    constexpr float kMaxRise = 64.f;
-    float m_ref = -INFINITY;
-    float l_run;       // this lane's share of sum_j p_j
-    f32x4 oacc[4][4];  // O^T of this wave: [16-dim block of its 64 dims][16-head block]
-
-    for (;;) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                oacc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // the accumulators live in AGPRs from the start, so the loop
-                // does not move them between register files each iteration
-                asm volatile("" : "+a"(oacc[i][hb]));
-            }
-        l_run = 0.f;
-        bool have_ref = m_ref != -INFINITY;  // set by an earlier pass (the same in every lane)
-        bool restart = false;
-
-#pragma unroll
-        for (int t = 0; t < NST - 1; ++t)
-            if (t < ntiles) issue(t);
-
-        for (int it = 0; it < ntiles; ++it) {
-            wait_for_tile(min(NST - 2, ntiles - 1 - it));
-            __syncthreads();  // tile `it` is in LDS for every wave; stage (it-1)%NST is free
-            if (it + NST - 1 < ntiles) issue(it + NST - 1);
-
-            const lds_u8* st = lds + (it % NST) * STAGE;
-            const lds_u8* rt = rowtab + 4 * it * kTile;
-            // validity of this lane's accumulator tokens, and of the other half's
-            const i32x4 vown = lds_load<i32x4>(rt + 4 * tC);
-            const i32x4 voth = lds_load<i32x4>(rt + 4 * (tC ^ 16));
-
-            // ---- S^T = K . Q^T for the 16 tokens of this wave's half
-            f32x4 s;
-            f32x4 sc[4];  // fp8: sc[j][grp] = scale of group grp of accumulator token tC + j
-            if (FMT == 0) {
-                constexpr int PF = 6;  // K operands in flight
-                bf16x8 ka[PF];
-                f32x4 se = f32x4{0.f, 0.f, 0.f, 0.f}, so = se;  // even / odd k-steps (two MFMA chains)
-#pragma unroll
-                for (int kk = 0; kk < PF; ++kk) ka[kk] = lds_load<bf16x8>(st + qk[kk & 1] + (kk >> 1) * kTile * 128);
-#pragma unroll
-                for (int kk = 0; kk < 18; ++kk) {
-                    const int sl = kk % PF;
-                    if (kk & 1)
-                        so = mfma16(ka[sl], qreg[kk], so);
-                    else
-                        se = mfma16(ka[sl], qreg[kk], se);
-                    if (kk + PF < 18) {
-                        const int kn = kk + PF;
-                        ka[sl] = lds_load<bf16x8>(st + qk[kn & 1] + (kn >> 1) * kTile * 128);
-                    }
-                }
-                // PF reads first, then MFMA / read pairs
-                __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-                for (int i = 0; i < 18 - PF; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
-                s = se + so;
-            } else {
-                // 10 load units: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
-                constexpr int PF = 5;
-                u32x4 ka[PF];
-                auto unit_off = [&](int u) {
-                    return u < 2 ? qk[u] + 4 * kTile * 128 : qk[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
-                };
-                const lds_u8* scl = st + NBANDS * kTile * 128;
-#pragma unroll
-                for (int u = 0; u < PF; ++u) ka[u] = lds_load<u32x4>(st + unit_off(u));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sc[j] = lds_load<f32x4>(scl + 16 * (tC + j));
-                s = f32x4{0.f, 0.f, 0.f, 0.f};
-                f32x4 p = s;
-#pragma unroll
-                for (int u = 0; u < 10; ++u) {
-                    const int sl = u % PF;
-                    if (u < 2) {
-                        s = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[16 + u], s);
-                    } else {
-                        const int grp = (u - 2) >> 1, pr = (u - 2) & 1;
-                        if (pr == 0) p = f32x4{0.f, 0.f, 0.f, 0.f};
-                        p = mfma16(e4m3x8_to_bf16(ka[sl][0], ka[sl][1]), qreg[4 * grp + 2 * pr], p);
-                        p = mfma16(e4m3x8_to_bf16(ka[sl][2], ka[sl][3]), qreg[4 * grp + 2 * pr + 1], p);
-                        if (pr == 1) {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) s[j] += sc[j][grp] * p[j];
-                        }
-                    }
-                    if (u + PF < 10) ka[sl] = lds_load<u32x4>(st + unit_off(u + PF));
-                }
-                // first PF units' reads and the scales, then per unit its MFMAs and the next unit's read
-                __builtin_amdgcn_sched_group_barrier(0x100, PF + 4, 0);
-#pragma unroll
-                for (int u = 0; u < 10 - PF; ++u) {
-                    if (u < 2)
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    else
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
-            }
-
-            // ---- mask, softmax weights (base 2)
-            float sv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sv[j] = vown[j] >= 0 ? s[j] * a.scale_log2 : -INFINITY;
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            bool rise = false;
-            if (!have_ref) {
-                // first tile with a valid token: the same tile in every wave (each
-                // lane group sees 4 tokens of both halves, so the vote covers all 32)
-                const bool any_valid = vown[0] >= 0 || vown[1] >= 0 || vown[2] >= 0 || vown[3] >= 0 ||
-                                       voth[0] >= 0 || voth[1] >= 0 || voth[2] >= 0 || voth[3] >= 0;
-                if (__any(any_valid)) {
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_TMAX + 4 * (tb * kHeads + head)) = mx;
-                    __syncthreads();
-                    m_ref = fmaxf(mx, lds_load<float>(aux + AUX_TMAX + 4 * ((tb ^ 1) * kHeads + head)));
-                    have_ref = true;
-                }
-            } else if (mx > m_ref + kMaxRise) {  // lane-local test; the restart is decided after PV
-                rise = true;
-                m_ref = fmaxf(m_ref, mx);  // (reconciled across the head's lanes on restart)
-            }
-            const float m_use = have_ref ? m_ref : 0.f;
-            // The denominator sums the fp32 weights; the PV product takes them
-            // rounded to bf16 once (for fp8 rows after multiplying by the
-            // token's scale of each 128-group, one copy per group).
-            float pf[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pf[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
-            l_run += (pf[0] + pf[1]) + (pf[2] + pf[3]);
-            if (FMT == 0) {
-                bf16x4 pb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pb[j] = (__bf16)pf[j];
-                *(__attribute__((address_space(3))) bf16x4*)p_mine = pb;
-            } else {
-#pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    bf16x4 pg;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) pg[j] = (__bf16)(pf[j] * sc[j][grp]);
-                    *(__attribute__((address_space(3))) bf16x4*)(p_mine + grp * kPBytesPerCopy) = pg;
-                }
-            }
-            const int any_rise = __any(rise) ? 1 : 0;
-            if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 4 * wave) = any_rise;
-            __syncthreads();  // P and the rise flags of every wave are visible
-            const i32x4 fl0 = lds_load<i32x4>(aux + AUX_FLAG);
-            const i32x4 fl1 = lds_load<i32x4>(aux + AUX_FLAG + 16);
-
-            // ---- O^T[this wave's 64 dims, all heads] += V^T . P^T
-            bf16x8 pbh[4];  // P^T of head block hb (fp8: scaled for this wave's group)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(p_read + hb * 1024);
-            if (FMT == 0) {
-                bf16x4 va[4], vb[4];
-                auto tr = [&](int m, int blk) {
-                    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (__attribute__((address_space(3))) bf16x4*)(st + pv[4 * blk + m]));
-                };
-#pragma unroll
-                for (int m = 0; m < 4; ++m) { va[m] = tr(m, 0); vb[m] = tr(m, 1); }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    // (the bf16-typed transpose read: rebuilding the operand element
-                    // by element from the i16-typed form is miscompiled)
-                    const bf16x8 av = __builtin_shufflevector(va[m], vb[m], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = mfma16(av, pbh[hb], oacc[m][hb]);
-                }
-            } else {
-                i32x2 raw[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    raw[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[m]));
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const bf16x8 av = e4m3x8_to_bf16((unsigned)raw[m][0], (unsigned)raw[m][1]);
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = mfma16(av, pbh[hb], oacc[m][hb]);
-                }
-            }
-
-            if ((fl0[0] | fl0[1] | fl0[2] | fl0[3]) | (fl1[0] | fl1[1] | fl1[2] | fl1[3])) {
-                restart = true;  // rare: restart with raised references
-                break;
-            }
-        }
-        if (!restart) break;
-        // the head's reference: max over its lanes in this wave and the other half
-        m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 16));
-        m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 32));
-        wait_vmcnt<0>();  // drain the stage DMAs still in flight
-        if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_TMAX + 4 * (tb * kHeads + head)) = m_ref;
-        __syncthreads();  // every wave has left the loop; stages may be refilled
-        m_ref = fmaxf(m_ref, lds_load<float>(aux + AUX_TMAX + 4 * ((tb ^ 1) * kHeads + head)));
-        __syncthreads();  // tmax is read before the next pass may write it
-    }
-
-    // ---- epilogue: denominators, lse, normalised output
-    float l_half = l_run;
-    l_half += __shfl_xor(l_half, 16);
-    l_half += __shfl_xor(l_half, 32);
-    if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * (tb * kHeads + head)) = l_half;
-    __syncthreads();
-    if (tb == 0 && g == 0) {
-        const bool empty = (m_ref == -INFINITY);
-        const float l_tot = l_half + lds_load<float>(aux + AUX_DENOM + 4 * (kHeads + head));
-        const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * kLn2;
-        if (a.num_splits == 1)
-            a.lse[(int64_t)r * kHeads + head] = lse_v;
-        else
-            a.part_lse[((int64_t)sp * a.rows + r) * kHeads + head] = lse_v;
-    }
-    // The normalised output goes through the (now idle) stage ring, 32 heads at
-    // a time, so that every head's row is written to HBM with contiguous
-    // 1 KB stores.  Rows are padded by 16 bytes: the staging writes of a
-    // 16-lane group (16 heads, same dims) then fall on distinct banks.  (Every
-    // stage DMA has landed: the last loop iteration waited for all of them.)
+    // ---- output staging: the normalised output goes through the (then idle)
+    // stage ring, 32 heads at a time, so that every head's row is written to
+    // HBM with contiguous 1 KB stores.  Rows are padded by 16 bytes: the
+    // staging writes of a 16-lane group (16 heads, same dims) then fall on
+    // distinct banks.  The PV waves fill a half, then every wave stores 4 of
+    // its heads.
     constexpr int kRowPitch = 4 * kDv + 16;
     static_assert(32 * kRowPitch <= NST * STAGE, "staging area exceeds the stage ring");
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-            const int hb = 2 * half + hl;
-            const int h = 16 * hb + i16;
-            const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h) + lds_load<float>(aux + AUX_DENOM + 4 * (kHeads + h));
-            const float inv = (m_ref == -INFINITY || lt == 0.f) ? 0.f : 1.f / lt;
-            lds_u8* row = lds + (h - 32 * half) * kRowPitch + 4 * (64 * wave + 4 * g);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) *(__attribute__((address_space(3))) f32x4*)(row + 64 * m) = oacc[m][hb] * inv;
-        }
-        __syncthreads();
+    auto store_half = [&](int half) {
         // wave w stores heads 32*half + 4w .. 32*half + 4w + 3; lane l holds dims
         // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
 #pragma unroll
@@ -563,7 +217,398 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 *(f32x4*)(o + 256) = x1;
             }
         }
-        if (half == 0) __syncthreads();  // the staging rows are free again
+    };
+
+    // Every wave runs the same sequence of workgroup barriers: B0 (row table
+    // ready), P0 (tile 0 in LDS), E_k at the end of each step k in
+    // [0, ntiles], D (denominators), then two per output half.  In step k the
+    // QK waves turn tile k into softmax weights P(k) while the PV waves add
+    // tile k-1 to the output with P(k-1) and wait for tile k+1 to land.
+    if (wave < 4) {
+        // =================== QK waves: heads [16q, 16q + 16) ===================
+        const int q = wave;
+        const int head = 16 * q + i16;
+        // Q of `head` as the B operand of S^T = K . Q^T (8 dims of k-step kk per
+        // lane); for fp8 rows the c_kv dims of k-steps 2p and 2p+1 inside a
+        // 128-group are the two halves of one 16-byte run, so one LDS read
+        // feeds two k-steps.
+        bf16x8 qreg[18];
+        {
+            const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * kDqk;
+#pragma unroll
+            for (int kk = 0; kk < 18; ++kk) {
+                int d;
+                if (FMT == 0 || kk >= 16)
+                    d = 32 * kk + 8 * g;
+                else
+                    d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
+                qreg[kk] = *(const bf16x8*)(qh + d);
+            }
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qreg[kk]));  // Q stays in AGPRs
+        __syncthreads();  // B0
+
+        // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
+        // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
+        const int tokA0 = i16, tokA1 = 16 + i16;
+        const int tokC0 = 4 * g, tokC1 = 16 + 4 * g;
+        int qk0[2], qk1[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz(tokA0)) << 4);
+            qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz(tokA1)) << 4);
+        }
+        // P slot of this lane: (block q, group g, lane i16): its 8 weights are
+        // the k-slots 8g .. 8g + 7 of the PV B operand, i.e. tokens
+        // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
+        lds_u8* const p_mine = aux + ((q * 4 + g) * 16 + i16) * 16;  // + buffer (+ group copy for fp8)
+
+        // Online softmax of `head`, base 2.  Weights are taken against a
+        // reference maximum m_ref, set at the first tile with a valid token;
+        // it is raised only when a tile's maximum exceeds it by more than
+        // kMaxRise (weights up to 2^kMaxRise stay finite in fp32 and bf16), and
+        // then the denominator here and the output accumulators of the PV waves
+        // are rescaled by alpha = 2^(old - new).
+        constexpr float kMaxRise = 32.f;
+        float m_ref = -INFINITY;  // the same in the four lanes of the head
+        float l_run = 0.f;        // this lane's share of the denominator
+        bool ref_set = false;     // the same in every lane of the wave
+        __syncthreads();  // P0
+        for (int k = 0; k <= ntiles; ++k) {
+            int raised = 0;
+            if (k < ntiles) {
+                const lds_u8* st = lds + (k % NST) * STAGE;
+                const lds_u8* rt = rowtab + 4 * k * kTile;
+                const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
+                const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
+
+                // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
+                f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                f32x4 sc0[4], sc1[4];  // fp8: sc*[e][grp] = scale of group grp of accumulator token e
+                if (FMT == 0) {
+                    constexpr int PF = 4;  // k-steps of K operands in flight
+                    bf16x8 ka[PF], kb[PF];
+#pragma unroll
+                    for (int kk = 0; kk < PF; ++kk) {
+                        ka[kk] = lds_load<bf16x8>(st + qk0[kk & 1] + (kk >> 1) * kTile * 128);
+                        kb[kk] = lds_load<bf16x8>(st + qk1[kk & 1] + (kk >> 1) * kTile * 128);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 18; ++kk) {
+                        const int sl = kk % PF;
+                        s0 = mfma16(ka[sl], qreg[kk], s0);
+                        s1 = mfma16(kb[sl], qreg[kk], s1);
+                        if (kk + PF < 18) {
+                            const int kn = kk + PF;
+                            ka[sl] = lds_load<bf16x8>(st + qk0[kn & 1] + (kn >> 1) * kTile * 128);
+                            kb[sl] = lds_load<bf16x8>(st + qk1[kn & 1] + (kn >> 1) * kTile * 128);
+                        }
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+                    for (int i = 0; i < 18 - PF; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+                } else {
+                    // 10 load units per block: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
+                    constexpr int PF = 3;
+                    u32x4 ka[PF], kb[PF];
+                    auto unit_off = [&](int u, int blk) {
+                        const int* qo = blk == 0 ? qk0 : qk1;
+                        return u < 2 ? qo[u] + 4 * kTile * 128 : qo[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
+                    };
+                    const lds_u8* scl = st + NBANDS * kTile * 128;
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
+                        kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sc0[e] = lds_load<f32x4>(scl + 16 * (tokC0 + e));
+                        sc1[e] = lds_load<f32x4>(scl + 16 * (tokC1 + e));
+                    }
+                    f32x4 p0 = s0, p1 = s0;
+#pragma unroll
+                    for (int u = 0; u < 10; ++u) {
+                        const int sl = u % PF;
+                        if (u < 2) {
+                            s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[16 + u], s0);
+                            s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[16 + u], s1);
+                        } else {
+                            const int grp = (u - 2) >> 1, pr = (u - 2) & 1;
+                            if (pr == 0) { p0 = f32x4{0.f, 0.f, 0.f, 0.f}; p1 = p0; }
+                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][0], ka[sl][1]), qreg[4 * grp + 2 * pr], p0);
+                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][0], kb[sl][1]), qreg[4 * grp + 2 * pr], p1);
+                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][2], ka[sl][3]), qreg[4 * grp + 2 * pr + 1], p0);
+                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][2], kb[sl][3]), qreg[4 * grp + 2 * pr + 1], p1);
+                            if (pr == 1) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    s0[e] += sc0[e][grp] * p0[e];
+                                    s1[e] += sc1[e][grp] * p1[e];
+                                }
+                            }
+                        }
+                        if (u + PF < 10) {
+                            ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
+                            kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
+                        }
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF + 8, 0);
+#pragma unroll
+                    for (int u = 0; u < 10 - PF; ++u) {
+                        if (u < 2)
+                            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        else
+                            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+                }
+
+                // ---- mask, reference, softmax weights (base 2)
+                float sv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[e] = v0[e] >= 0 ? s0[e] * a.scale_log2 : -INFINITY;
+                    sv[4 + e] = v1[e] >= 0 ? s1[e] * a.scale_log2 : -INFINITY;
+                }
+                float mx = sv[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+                if (!ref_set) {
+                    // first tile with a valid token (the same tile for every head and wave)
+                    const bool any_valid = v0[0] >= 0 || v0[1] >= 0 || v0[2] >= 0 || v0[3] >= 0 || v1[0] >= 0 ||
+                                           v1[1] >= 0 || v1[2] >= 0 || v1[3] >= 0;
+                    if (__any(any_valid)) {
+                        mx = fmaxf(mx, __shfl_xor(mx, 16));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32));
+                        m_ref = mx;
+                        ref_set = true;
+                    }
+                } else if (__any(mx > m_ref + kMaxRise)) {  // rare: raise the references of this wave's heads
+                    mx = fmaxf(mx, __shfl_xor(mx, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    const bool up = mx > m_ref + kMaxRise;
+                    const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+                    m_ref = up ? mx : m_ref;
+                    l_run *= alpha;
+                    if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_ALPHA + (k & 1) * (kHeads * 4) + 4 * head) = alpha;
+                    raised = 1;
+                }
+                const float m_use = ref_set ? m_ref : 0.f;
+                // The denominator sums the fp32 weights; the PV product takes them
+                // rounded to bf16 once (for fp8 rows after multiplying by the
+                // token's scale of each 128-group, one copy per group).
+                float pf[8];
+                float psum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pf[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+                    psum += pf[e];
+                }
+                l_run += psum;
+                lds_u8* const pbuf = p_mine + (k & 1) * PBUF;
+                if (FMT == 0) {
+                    bf16x8 pb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pf[e];
+                    *(__attribute__((address_space(3))) bf16x8*)pbuf = pb;
+                } else {
+#pragma unroll
+                    for (int grp = 0; grp < 4; ++grp) {
+                        bf16x8 pg;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            pg[e] = (__bf16)(pf[e] * sc0[e][grp]);
+                            pg[4 + e] = (__bf16)(pf[4 + e] * sc1[e][grp]);
+                        }
+                        *(__attribute__((address_space(3))) bf16x8*)(pbuf + grp * kPBytesPerCopy) = pg;
+                    }
+                }
+            }
+            if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 16 * (k & 1) + 4 * q) = raised;
+            __syncthreads();  // E_k
+        }
+
+        // ---- denominator and lse of `head`
+        float l_tot = l_run;
+        l_tot += __shfl_xor(l_tot, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (g == 0) {
+            *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
+            const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+            if (a.num_splits == 1)
+                a.lse[(int64_t)r * kHeads + head] = lse_v;
+            else
+                a.part_lse[((int64_t)sp * a.rows + r) * kHeads + head] = lse_v;
+        }
+        __syncthreads();  // D
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads();  // the PV waves have staged this half
+            store_half(half);
+            if (half == 0) __syncthreads();  // the staging rows are free again
+        }
+    } else {
+        // ========= PV waves: value dims [128p, 128p + 128), all heads =========
+        const int p = wave - 4;
+        __syncthreads();  // B0
+
+        // gather: wave p moves tokens [8p, 8p + 8) of every tile, all bands
+        auto issue = [&](int tile) {
+            const unsigned sbase = lds0 + (unsigned)((tile % NST) * STAGE);
+            const int t = 8 * p + (lane >> 3);  // token of this lane within the tile
+            const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
+            const int chunk = (lane & 7) ^ swz(t);
+            const unsigned char* src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
+            const int bstride = row >= 0 ? 128 : 0;
+#pragma unroll
+            for (int bd = 0; bd < NBANDS; ++bd)
+                lds_dma16(src + bd * bstride, sbase + (unsigned)((bd * kTile + 8 * p) * 128));
+            if (FMT == 1) {
+                // fp32 scales: lanes 0..7 fetch the 16 bytes of tokens 8p + lane
+                const int t2 = 8 * p + (lane & 7);
+                const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
+                const unsigned char* s2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
+                if (lane < 8) lds_dma16(s2, sbase + (unsigned)(NBANDS * kTile * 128 + 8 * p * 16));
+            }
+        };
+
+        // V^T operand offsets: the k-slots 8g .. 8g + 7 of a lane are the tokens
+        // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 (the P operand order).
+        //   bf16: bands 2p, 2p + 1; lane i16 addresses token tok + (i16 >> 2), 4 dims
+        //         at 4(i16 & 3) of 16-dim block m; the transpose read hands lane i dim i.
+        //   fp8 : band p (the scale group), 16-dim block c; lane i16 addresses token
+        //         slot j = i16 >> 1, 8 dims at 8(i16 & 1).
+        int pv[8];
+        if (FMT == 0) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int ta = 16 * blk + 4 * g + (i16 >> 2);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    pv[4 * blk + m] = (2 * p * kTile + ta) * 128 + (((2 * m + ((i16 & 3) >> 1)) ^ swz(ta)) << 4) +
+                                      8 * (i16 & 1);
+            }
+        } else {
+            const int j = i16 >> 1;
+            const int ta = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) pv[c] = (p * kTile + ta) * 128 + ((c ^ swz(ta)) << 4) + 8 * (i16 & 1);
+        }
+        const lds_u8* const p_read = aux + (FMT == 0 ? 0 : p * kPBytesPerCopy) + lane * 16;  // + hb * 1024 + buffer
+
+        f32x4 oacc[8][4];  // O^T [16-dim block of this wave's 128 dims][16-head block]
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                oacc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                asm volatile("" : "+v"(oacc[i][hb]));  // accumulate in VGPRs (Q of the QK waves takes the AGPRs)
+            }
+        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
+        for (int t = 0; t < pro; ++t) issue(t);
+        if (ntiles > 0) wait_tiles<LPT>(pro - 1);  // tile 0 has landed
+        __syncthreads();  // P0
+        for (int k = 0; k <= ntiles; ++k) {
+            if (k >= 1) {
+                const int kp = (k - 1) & 1;
+                // heads whose reference was raised at tile k-1: rescale their accumulators first
+                const i32x4 fl = lds_load<i32x4>(aux + AUX_FLAG + 16 * kp);
+                if (fl[0] | fl[1] | fl[2] | fl[3]) {
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb)
+                        if (fl[hb]) {
+                            const float al = lds_load<float>(aux + AUX_ALPHA + kp * (kHeads * 4) + 4 * (16 * hb + i16));
+#pragma unroll
+                            for (int db = 0; db < 8; ++db) oacc[db][hb] *= al;
+                        }
+                }
+                // ---- O^T[this wave's 128 dims, all heads] += V^T . P^T over tile k-1
+                const lds_u8* st = lds + ((k - 1) % NST) * STAGE;
+                const lds_u8* pr = p_read + kp * PBUF;
+                bf16x8 pbh[4];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(pr + hb * 1024);
+                if (FMT == 0) {
+                    constexpr int PF = 3;  // 16-dim blocks of transpose reads in flight
+                    bf16x4 va[PF], vb[PF];
+                    auto tr = [&](int db, int blk) {
+                        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (__attribute__((address_space(3))) bf16x4*)(st + pv[4 * blk + (db & 3)] + (db >> 2) * kTile * 128));
+                    };
+#pragma unroll
+                    for (int db = 0; db < PF; ++db) { va[db] = tr(db, 0); vb[db] = tr(db, 1); }
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const int sl = db % PF;
+                        // (the bf16-typed transpose read: rebuilding the operand element
+                        // by element from the i16-typed form is miscompiled)
+                        const bf16x8 av = __builtin_shufflevector(va[sl], vb[sl], 0, 1, 2, 3, 4, 5, 6, 7);
+                        if (db + PF < 8) { va[sl] = tr(db + PF, 0); vb[sl] = tr(db + PF, 1); }
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PF, 0);
+#pragma unroll
+                    for (int db = 0; db < 8 - PF; ++db) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+                } else {
+                    constexpr int PF = 4;
+                    i32x2 raw[PF];
+                    auto tr = [&](int db) {
+                        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
+                    };
+#pragma unroll
+                    for (int db = 0; db < PF; ++db) raw[db] = tr(db);
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const int sl = db % PF;
+                        const bf16x8 av = e4m3x8_to_bf16((unsigned)raw[sl][0], (unsigned)raw[sl][1]);
+                        if (db + PF < 8) raw[sl] = tr(db + PF);
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4 + PF, 0);
+#pragma unroll
+                    for (int db = 0; db < 8 - PF; ++db) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+                }
+            }
+            if (k + 1 < ntiles) wait_tiles<LPT>(min(NST - 3, ntiles - 2 - k));  // tile k+1 has landed
+            __syncthreads();  // E_k
+            if (k + NST - 1 < ntiles) issue(k + NST - 1);  // into the stage of tile k-1, now free
+        }
+        __syncthreads();  // D
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int hb = 2 * half + hl;
+                const int h = 16 * hb + i16;
+                const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h);
+                const float inv = lt == 0.f ? 0.f : 1.f / lt;
+                lds_u8* row = lds + (h - 32 * half) * kRowPitch + 4 * (128 * p + 4 * g);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    *(__attribute__((address_space(3))) f32x4*)(row + 64 * db) = oacc[db][hb] * inv;
+            }
+            __syncthreads();  // this half is staged
+            store_half(half);
+            if (half == 0) __syncthreads();  // the staging rows are free again
+        }
     }
 }
 

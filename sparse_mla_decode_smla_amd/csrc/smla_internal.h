@@ -15,9 +15,11 @@ constexpr int kDr = kDqk - kDv;  // rope width
 constexpr int kBlock = 64;       // tokens per cache block
 
 // Workgroup shape of the partial-attention kernel: 8 waves of 64 lanes, two
-// per SIMD.  For QK^T wave w owns heads [16(w%4), 16(w%4) + 16) and tokens
-// [16(w/4), 16(w/4) + 16) of a tile; for PV it owns value dims
-// [64w, 64w + 64) of all 64 heads.
+// per SIMD, in two roles that work on consecutive tiles at the same time.
+//   QK waves 0-3: wave w computes the scores and softmax weights of heads
+//     [16w, 16w + 16) over all 32 tokens of tile k;
+//   PV waves 4-7: wave 4+p accumulates value dims [128p, 128p + 128) of all
+//     64 heads over tile k-1, and issues the tile gathers.
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;        // tokens gathered per pipeline stage
@@ -37,22 +39,23 @@ constexpr int kBandsFp8 = 5;
 constexpr int kStageBytesBf16 = kBandsBf16 * kTile * 128;
 constexpr int kStageBytesFp8 = kBandsFp8 * kTile * 128 + kTile * 16;
 constexpr int kStagesBf16 = 4;
-constexpr int kStagesFp8 = 6;
+constexpr int kStagesFp8 = 5;
 
-// Exchange area after the stage ring:
-//   P      the softmax weights of a tile, bf16, in the order of the PV
-//          B operand: [16-head block][4 lane groups][16 heads] x 16 bytes
-//          (8 bytes from each token half); for fp8 rows one copy per
-//          128-group with that group's per-token scale folded in;
-//   flags  one restart flag per wave;
-//   tmax   per-head maxima of the two token halves [2][64] fp32;
-//   denom  per-head softmax denominators of the two token halves [2][64] fp32.
+// Exchange area after the stage ring, double-buffered by tile parity:
+//   P      the softmax weights of a tile, bf16, in the order of the PV B
+//          operand: [16-head block][4 lane groups][16 heads] x 16 bytes; for
+//          fp8 rows one copy per 128-group with that group's per-token scale
+//          folded in;
+//   alpha  per-head factors [64] fp32 that rescale the output accumulators
+//          when a head's reference maximum was raised at that tile;
+//   flags  one int per QK wave: it raised a reference at that tile;
+// then denom, the per-head softmax denominators [64] fp32.
 constexpr int kPBytesPerCopy = kHeads * kTile * 2;
-inline constexpr int aux_p_bytes(int kv_format) { return kv_format == 0 ? kPBytesPerCopy : 4 * kPBytesPerCopy; }
-inline constexpr int aux_flag_offset(int kv_format) { return aux_p_bytes(kv_format); }
-inline constexpr int aux_tmax_offset(int kv_format) { return aux_flag_offset(kv_format) + 64; }
-inline constexpr int aux_denom_offset(int kv_format) { return aux_tmax_offset(kv_format) + 2 * kHeads * 4; }
-inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + 2 * kHeads * 4; }
+inline constexpr int aux_p_buffer_bytes(int kv_format) { return kv_format == 0 ? kPBytesPerCopy : 4 * kPBytesPerCopy; }
+inline constexpr int aux_alpha_offset(int kv_format) { return 2 * aux_p_buffer_bytes(kv_format); }
+inline constexpr int aux_flag_offset(int kv_format) { return aux_alpha_offset(kv_format) + 2 * kHeads * 4; }
+inline constexpr int aux_denom_offset(int kv_format) { return aux_flag_offset(kv_format) + 2 * 16; }
+inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + kHeads * 4; }
 
 constexpr int kLdsLimit = 160 * 1024;  // bytes of LDS a gfx950 workgroup may use
 
