@@ -139,9 +139,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int NST = FMT == 0 ? kStagesBf16 : kStagesFp8;
     constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : kRowBytesFp8;
     constexpr int NBANDS = FMT == 0 ? kBandsBf16 : kBandsFp8;
-    constexpr int LPT = NBANDS + (FMT == 0 ? 0 : 1);  // DMA instructions per PV wave per tile
     constexpr int PBUF = aux_p_buffer_bytes(FMT);
-    static_assert(NST >= 3 && NST - 3 <= 4, "stage ring depth outside what the waits cover");
+    static_assert(NST >= 2 && NST - 2 <= 4, "stage ring depth outside what the waits cover");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_generic[];
     lds_u8* lds = (lds_u8*)smem_generic;
@@ -219,11 +218,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
 
+    // ---- gather: the PV wave 4+o moves the tokens [8o, 8o + 8) of each tile,
+    // all bands (and, for fp8 rows, the fp32 scales, lanes 0..7 fetching the
+    // 16 bytes of their token), so it issues a fixed number of DMA
+    // instructions per tile and counts them itself.  (The split between the
+    // roles is a parameter: LPT_QK bands of each slice could go to the QK
+    // waves instead; measured, that was not faster.)  A tile's DMAs are
+    // prepared (row-table read, addresses) first and issued one at a time, so
+    // they can be spread between MFMAs.
+    constexpr int LPT_PV = FMT == 0 ? 9 : 6;
+    constexpr int LPT_QK = 0;
+    const int oct = wave & 3;
+    const int band0 = wave < 4 ? LPT_PV : 0;  // first band of this wave
+    struct Gather {
+        const unsigned char* src;   // this lane's 16 bytes of band 0 (or the zero chunk)
+        const unsigned char* src2;  // fp8: this lane's scale bytes
+        int bstride;                // 128, or 0 for a masked token
+        unsigned sbase;             // LDS byte address of the stage
+    };
+    auto prepare = [&](int tile) {
+        Gather gt;
+        gt.sbase = lds0 + (unsigned)((tile % NST) * STAGE);
+        const int t = 8 * oct + (lane >> 3);  // token of this lane within the tile
+        const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
+        const int chunk = (lane & 7) ^ swz(t);
+        gt.src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
+        gt.bstride = row >= 0 ? 128 : 0;
+        gt.src2 = kZeroChunk;
+        if (FMT == 1) {
+            const int t2 = 8 * oct + (lane & 7);
+            const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
+            gt.src2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
+        }
+        return gt;
+    };
+    auto issue_one = [&](const Gather& gt, int i) {  // DMA i of this wave's share of a tile
+        const int bd = band0 + i;
+        if (bd < NBANDS)
+            lds_dma16(gt.src + bd * gt.bstride, gt.sbase + (unsigned)((bd * kTile + 8 * oct) * 128));
+        else if (lane < 8)
+            lds_dma16(gt.src2, gt.sbase + (unsigned)(NBANDS * kTile * 128 + 8 * oct * 16));
+    };
+    static_assert(LPT_PV + LPT_QK == NBANDS + (FMT == 0 ? 0 : 1), "the two roles cover every band of a slice");
+
     // Every wave runs the same sequence of workgroup barriers: B0 (row table
     // ready), P0 (tile 0 in LDS), E_k at the end of each step k in
-    // [0, ntiles], D (denominators), then two per output half.  In step k the
-    // QK waves turn tile k into softmax weights P(k) while the PV waves add
-    // tile k-1 to the output with P(k-1) and wait for tile k+1 to land.
+    // [0, ntiles], D (denominators), then three for the output halves.  In
+    // step k the QK waves turn tile k into softmax weights P(k); the PV waves
+    // add tile k-1 to the output with P(k-1) (from V held in registers) while
+    // refilling the stage of tile k-1 with tile k + NST - 1, copy their V slice
+    // of tile k into registers and wait for tile k+1 to land.  NST - 2 tiles
+    // beyond the next one are in flight while a tile is computed.
     if (wave < 4) {
         // =================== QK waves: heads [16q, 16q + 16) ===================
         const int q = wave;
@@ -247,7 +292,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         wait_vmcnt<0>();
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qreg[kk]));  // Q stays in AGPRs
+        for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
         __syncthreads();  // B0
 
         // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
@@ -275,9 +320,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         float m_ref = -INFINITY;  // the same in the four lanes of the head
         float l_run = 0.f;        // this lane's share of the denominator
         bool ref_set = false;     // the same in every lane of the wave
+        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
+        if (LPT_QK > 0) {
+            for (int t = 0; t < pro; ++t) {
+                const Gather gt = prepare(t);
+#pragma unroll
+                for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+            }
+            if (ntiles > 0) wait_tiles<LPT_QK>(pro - 1);  // this wave's part of tile 0 has landed
+        }
         __syncthreads();  // P0
         for (int k = 0; k <= ntiles; ++k) {
             int raised = 0;
+            // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
+            if (LPT_QK > 0 && k + NST - 1 < ntiles) {
+                const Gather gt = prepare(k + NST - 1);
+#pragma unroll
+                for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+            }
             if (k < ntiles) {
                 const lds_u8* st = lds + (k % NST) * STAGE;
                 const lds_u8* rt = rowtab + 4 * k * kTile;
@@ -433,6 +493,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
             }
             if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 16 * (k & 1) + 4 * q) = raised;
+            if (LPT_QK > 0 && k + 1 < ntiles) wait_tiles<LPT_QK>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
         }
 
@@ -459,26 +520,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // ========= PV waves: value dims [128p, 128p + 128), all heads =========
         const int p = wave - 4;
         __syncthreads();  // B0
-
-        // gather: wave p moves tokens [8p, 8p + 8) of every tile, all bands
-        auto issue = [&](int tile) {
-            const unsigned sbase = lds0 + (unsigned)((tile % NST) * STAGE);
-            const int t = 8 * p + (lane >> 3);  // token of this lane within the tile
-            const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
-            const int chunk = (lane & 7) ^ swz(t);
-            const unsigned char* src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
-            const int bstride = row >= 0 ? 128 : 0;
-#pragma unroll
-            for (int bd = 0; bd < NBANDS; ++bd)
-                lds_dma16(src + bd * bstride, sbase + (unsigned)((bd * kTile + 8 * p) * 128));
-            if (FMT == 1) {
-                // fp32 scales: lanes 0..7 fetch the 16 bytes of tokens 8p + lane
-                const int t2 = 8 * p + (lane & 7);
-                const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
-                const unsigned char* s2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
-                if (lane < 8) lds_dma16(s2, sbase + (unsigned)(NBANDS * kTile * 128 + 8 * p * 16));
-            }
-        };
 
         // V^T operand offsets: the k-slots 8g .. 8g + 7 of a lane are the tokens
         // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 (the P operand order).
@@ -510,13 +551,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) {
                 oacc[i][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                asm volatile("" : "+v"(oacc[i][hb]));  // accumulate in VGPRs (Q of the QK waves takes the AGPRs)
+                asm volatile("" : "+v"(oacc[i][hb]));
             }
+        // This wave's V^T slice of a tile is copied from LDS into registers in
+        // the step that gathers the tile, so the stage is free again at the end
+        // of that step although the product runs one step later.
+        //   bf16: va/vb[db] = transpose reads of 16-dim block db, tokens of block 0 / 1
+        //   fp8 : vr[db] = 8-bit transpose read of 16-dim block db
+        bf16x4 va[8], vb[8];
+        i32x2 vr[8];
+        auto load_v = [&](const lds_u8* st) {
+            if (FMT == 0) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    va[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + (db >> 2) * kTile * 128));
+                    vb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4*)(st + pv[4 + (db & 3)] + (db >> 2) * kTile * 128));
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    vr[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
+            }
+        };
+
         const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
-        for (int t = 0; t < pro; ++t) issue(t);
-        if (ntiles > 0) wait_tiles<LPT>(pro - 1);  // tile 0 has landed
+        for (int t = 0; t < pro; ++t) {
+            const Gather gt = prepare(t);
+#pragma unroll
+            for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
+        }
+        if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
         __syncthreads();  // P0
         for (int k = 0; k <= ntiles; ++k) {
+            // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
+            const bool refill = k + NST - 1 < ntiles;
+            Gather gt;
+            if (refill) gt = prepare(k + NST - 1);
             if (k >= 1) {
                 const int kp = (k - 1) & 1;
                 // heads whose reference was raised at tile k-1: rescale their accumulators first
@@ -530,66 +602,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                             for (int db = 0; db < 8; ++db) oacc[db][hb] *= al;
                         }
                 }
-                // ---- O^T[this wave's 128 dims, all heads] += V^T . P^T over tile k-1
-                const lds_u8* st = lds + ((k - 1) % NST) * STAGE;
+                // ---- O^T[this wave's 128 dims, all heads] += V^T . P^T over tile k-1,
+                // with the refill DMAs between its MFMAs
                 const lds_u8* pr = p_read + kp * PBUF;
                 bf16x8 pbh[4];
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(pr + hb * 1024);
-                if (FMT == 0) {
-                    constexpr int PF = 3;  // 16-dim blocks of transpose reads in flight
-                    bf16x4 va[PF], vb[PF];
-                    auto tr = [&](int db, int blk) {
-                        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (__attribute__((address_space(3))) bf16x4*)(st + pv[4 * blk + (db & 3)] + (db >> 2) * kTile * 128));
-                    };
 #pragma unroll
-                    for (int db = 0; db < PF; ++db) { va[db] = tr(db, 0); vb[db] = tr(db, 1); }
+                for (int db = 0; db < 8; ++db) {
+                    // (bf16: the bf16-typed transpose read; rebuilding the operand element
+                    // by element from the i16-typed form is miscompiled)
+                    const bf16x8 av = FMT == 0 ? __builtin_shufflevector(va[db], vb[db], 0, 1, 2, 3, 4, 5, 6, 7)
+                                               : e4m3x8_to_bf16((unsigned)vr[db][0], (unsigned)vr[db][1]);
 #pragma unroll
-                    for (int db = 0; db < 8; ++db) {
-                        const int sl = db % PF;
-                        // (the bf16-typed transpose read: rebuilding the operand element
-                        // by element from the i16-typed form is miscompiled)
-                        const bf16x8 av = __builtin_shufflevector(va[sl], vb[sl], 0, 1, 2, 3, 4, 5, 6, 7);
-                        if (db + PF < 8) { va[sl] = tr(db + PF, 0); vb[sl] = tr(db + PF, 1); }
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PF, 0);
-#pragma unroll
-                    for (int db = 0; db < 8 - PF; ++db) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
-                } else {
-                    constexpr int PF = 4;
-                    i32x2 raw[PF];
-                    auto tr = [&](int db) {
-                        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
-                    };
-#pragma unroll
-                    for (int db = 0; db < PF; ++db) raw[db] = tr(db);
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) {
-                        const int sl = db % PF;
-                        const bf16x8 av = e4m3x8_to_bf16((unsigned)raw[sl][0], (unsigned)raw[sl][1]);
-                        if (db + PF < 8) raw[sl] = tr(db + PF);
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x100, 4 + PF, 0);
-#pragma unroll
-                    for (int db = 0; db < 8 - PF; ++db) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
+                    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
+                    if (refill && db < LPT_PV) issue_one(gt, db);
                 }
+                if (refill) {
+#pragma unroll
+                    for (int i = 8; i < LPT_PV; ++i) issue_one(gt, i);
+                }
+            } else if (refill) {
+#pragma unroll
+                for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
             }
-            if (k + 1 < ntiles) wait_tiles<LPT>(min(NST - 3, ntiles - 2 - k));  // tile k+1 has landed
+            if (k < ntiles) load_v(lds + (k % NST) * STAGE);
+            if (k + 1 < ntiles) wait_tiles<LPT_PV>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
-            if (k + NST - 1 < ntiles) issue(k + NST - 1);  // into the stage of tile k-1, now free
         }
         __syncthreads();  // D
 #pragma unroll

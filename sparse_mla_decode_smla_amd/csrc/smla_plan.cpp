@@ -3,12 +3,15 @@
 // The split count follows the occupancy argument of "The Moment of Truth:
 // Analyzing a Custom MMA Kernel's Performance on Blackwell GPUs" ("The
 // Occupancy Problem: A Deeper Dive", "The Split-K Solution: Reasoning About
-// the Fix"): one workgroup per (row, head group) leaves most of the GPU idle
-// at small batch, so the top-k list of each row is cut into parts until the
-// grid covers the compute units, and the choice depends only on the problem
-// shape so that a captured launch stays valid for its batch bucket.
+// the Fix"): one workgroup per row leaves most of the GPU idle at small
+// batch, so the top-k list of each row is cut into parts; here the count
+// minimises a cost model of both kernels (more parts fill more compute units
+// but write and re-read more partial results), and it depends only on the
+// problem shape so that a captured launch stays valid for its batch bucket.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -32,6 +35,47 @@ int query_cu_count(int* out) {
     if (dev < 64) cached[dev] = n;
     *out = n;
     return 0;
+}
+
+// Estimated time (us) of one call with S parts per row, from a model fitted
+// to measurements of the two kernels on MI355X (256 CUs):
+//   - a workgroup gathers its part at about 30 GB/s per CU, and the whole
+//     launch at most at about 5 TB/s; a 32-token tile costs about 0.55 us of
+//     compute (bf16 rows) or 1.7 us (fp8 rows, widened in registers); the
+//     partial kernel pays about 6 us of launch, prologue and epilogue;
+//   - with S > 1 every part writes 64 x 512 fp32 outputs (128 KiB) per row,
+//     which the combine kernel reads back: both move at about 5 TB/s, and the
+//     combine pays about 3 us plus 0.08 us per part (its load batches).
+// Workgroups beyond one per CU run in further rounds.
+double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus) {
+    const double row_bytes = p.kv_format == SMLA_KV_BF16 ? smla::kRowBytesBf16 : smla::kRowBytesFp8;
+    const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.55 : 1.7;
+    const int tps = (tiles + S - 1) / S;
+    const double wgs = (double)rows * S;
+    const double rounds = std::ceil(wgs / cus);
+    const double gathered = (double)rows * p.topk * row_bytes;       // upper bound: every entry valid
+    const double per_wg = (double)tps * smla::kTile * row_bytes;
+    const double t_gather = std::max(per_wg / 30e3 * rounds, gathered / 5e6);  // bytes / (bytes per us)
+    const double t_compute = t_tile * tps * rounds;
+    const double partial = S > 1 ? wgs * smla::kHeads * smla::kDv * 4.0 : 0.0;
+    double t = 6.0 + std::max(t_gather, t_compute) + partial / 5e6;
+    if (S > 1) t += 3.0 + partial / 5e6 + 0.08 * S;
+    return t;
+}
+
+int choose_splits(const smla_problem_t& p, int rows, int tiles, int cap_tiles, int cus) {
+    if (rows <= 0 || tiles <= 1) return 1;
+    const int min_s = (tiles + cap_tiles - 1) / cap_tiles;  // parts small enough for the LDS row table
+    int best = min_s;
+    double best_t = estimate_us(p, rows, tiles, min_s, cus);
+    for (int S = min_s + 1; S <= tiles; ++S) {
+        const double t = estimate_us(p, rows, tiles, S, cus);
+        if (t < best_t) {
+            best_t = t;
+            best = S;
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -61,9 +105,7 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
     if (p.force_splits > 0) {
         splits = p.force_splits;
     } else {
-        // Enough parts for about one workgroup per compute unit, never more
-        // parts than tiles.
-        splits = rows > 0 ? (cus + rows - 1) / rows : 1;
+        splits = choose_splits(p, rows, tiles, cap_tiles, cus);
     }
     if (splits > tiles) splits = tiles;
     if (splits < 1) splits = 1;
