@@ -555,40 +555,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         // This wave's V^T slice of a tile is copied from LDS into registers in
         // the step that gathers the tile, so the stage is free again at the end
-        // of that step although the product runs one step later.
+        // of that step although the product runs one step later.  Two register
+        // buffers alternate: a step first copies tile k (the QK waves' MFMAs
+        // run meanwhile), then multiplies tile k-1 (overlapping the QK waves'
+        // softmax).
         //   bf16: va/vb[db] = transpose reads of 16-dim block db, tokens of block 0 / 1
         //   fp8 : vr[db] = 8-bit transpose read of 16-dim block db
-        bf16x4 va[8], vb[8];
-        i32x2 vr[8];
-        auto load_v = [&](const lds_u8* st) {
+        struct VSlice {
+            bf16x4 va[8], vb[8];
+            i32x2 vr[8];
+        };
+        auto load_v = [&](VSlice& v, const lds_u8* st) {
             if (FMT == 0) {
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
-                    va[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    v.va[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + (db >> 2) * kTile * 128));
-                    vb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    v.vb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4*)(st + pv[4 + (db & 3)] + (db >> 2) * kTile * 128));
                 }
             } else {
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-                    vr[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
+                    v.vr[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
             }
         };
 
-        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
-        for (int t = 0; t < pro; ++t) {
-            const Gather gt = prepare(t);
-#pragma unroll
-            for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
-        }
-        if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
-        __syncthreads();  // P0
-        for (int k = 0; k <= ntiles; ++k) {
+        // step k: `cur` holds tile k-1's slice, `nxt` receives tile k's
+        auto step = [&](int k, VSlice& cur, VSlice& nxt) {
             // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
             const bool refill = k + NST - 1 < ntiles;
             Gather gt;
             if (refill) gt = prepare(k + NST - 1);
+            if (k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);
             if (k >= 1) {
                 const int kp = (k - 1) & 1;
                 // heads whose reference was raised at tile k-1: rescale their accumulators first
@@ -612,8 +611,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int db = 0; db < 8; ++db) {
                     // (bf16: the bf16-typed transpose read; rebuilding the operand element
                     // by element from the i16-typed form is miscompiled)
-                    const bf16x8 av = FMT == 0 ? __builtin_shufflevector(va[db], vb[db], 0, 1, 2, 3, 4, 5, 6, 7)
-                                               : e4m3x8_to_bf16((unsigned)vr[db][0], (unsigned)vr[db][1]);
+                    const bf16x8 av = FMT == 0 ? __builtin_shufflevector(cur.va[db], cur.vb[db], 0, 1, 2, 3, 4, 5, 6, 7)
+                                               : e4m3x8_to_bf16((unsigned)cur.vr[db][0], (unsigned)cur.vr[db][1]);
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
                     if (refill && db < LPT_PV) issue_one(gt, db);
@@ -626,10 +625,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
             }
-            if (k < ntiles) load_v(lds + (k % NST) * STAGE);
             if (k + 1 < ntiles) wait_tiles<LPT_PV>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
+        };
+
+        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
+        for (int t = 0; t < pro; ++t) {
+            const Gather gt = prepare(t);
+#pragma unroll
+            for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
         }
+        if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
+        __syncthreads();  // P0
+        VSlice v0, v1;
+        int k = 0;
+        for (; k + 1 <= ntiles; k += 2) {
+            step(k, v1, v0);
+            step(k + 1, v0, v1);
+        }
+        if (k <= ntiles) step(k, v1, v0);
         __syncthreads();  // D
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
