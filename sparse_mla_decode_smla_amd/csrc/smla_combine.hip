@@ -11,8 +11,8 @@
 // accumulated in fp32 and rounded to bf16 at the store.  A pair whose parts
 // are all empty gets out = 0 and lse = -inf.
 //
-// One wave per pair.  The weights of all parts are computed once, lane i
-// holding part i (then i + 64, ...), with wave-wide max / sum reductions;
+// One to four waves per pair.  The weights of all parts are computed with
+// lane i holding part i (then i + 64, ...) and wave-wide max / sum reductions;
 // the output loop then streams the parts' rows with 16-byte loads, lane l
 // owning 8 consecutive value dims, in batches of 16, 8, 4 or 1 parts (fitting
 // S exactly) whose loads are all issued before any is consumed, so a pair
@@ -66,15 +66,21 @@ __device__ __forceinline__ void add_parts(const float* base, int64_t part_stride
     }
 }
 
-// d_v == 512: lane l owns dims [8l, 8l + 8).  Grid: one 64-thread workgroup per pair.
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_out,
-                                                     const float* __restrict__ part_lse, int num_splits,
-                                                     int64_t pairs, uint16_t* __restrict__ out,
-                                                     float* __restrict__ lse) {
+// d_v == 512: lane l owns dims [8l, 8l + 8).  Grid: one workgroup of NW waves
+// per pair; wave w adds the parts of the w-th of NW contiguous ranges and
+// waves 1..NW-1 hand their sums to wave 0 through LDS.  Several waves per pair
+// put more loads in flight when there are few pairs (small batch).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void combine_kernel(const float* __restrict__ part_out,
+                                                          const float* __restrict__ part_lse, int num_splits,
+                                                          int64_t pairs, uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+    __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][2][64];
     const int64_t pair = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...)
+    // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...), in every wave
     float M = -INFINITY;
     for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
     M = wave_max(M);
@@ -90,21 +96,36 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 
     f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     if (total != -INFINITY) {
+        const int per_w = (num_splits + NW - 1) / NW;
+        const int lo = min(num_splits, w * per_w), hi = min(num_splits, lo + per_w);
         const float* base = part_out + pair * kDv + 8 * lane;
         const int64_t part_stride = pairs * kDv;
-        for (int s0 = 0; s0 < num_splits; s0 += 64) {
-            // weight of part s0 + lane (0 for an empty part or past the end)
-            float w = 0.f;
-            if (s0 + lane < num_splits) {
+        for (int s0 = lo; s0 < hi; s0 += 64) {
+            // weight of part s0 + lane (0 for an empty part or past the range)
+            float wt = 0.f;
+            if (s0 + lane < hi) {
                 const float l = part_lse[(int64_t)(s0 + lane) * pairs + pair];
-                w = l == -INFINITY ? 0.f : expf(l - total);
+                wt = l == -INFINITY ? 0.f : expf(l - total);
             }
-            const int n = min(64, num_splits - s0);
+            const int n = min(64, hi - s0);
             int j0 = 0;
-            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, w, acc0, acc1);
-            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, w, acc0, acc1); j0 += 8; }
-            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, w, acc0, acc1); j0 += 4; }
-            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, w, acc0, acc1);
+            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
+            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
+            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+        }
+    }
+    if (NW > 1) {
+        if (w > 0) {
+            red[w - 1][0][lane] = acc0;
+            red[w - 1][1][lane] = acc1;
+        }
+        __syncthreads();
+        if (w > 0) return;
+#pragma unroll
+        for (int i = 0; i < NW - 1; ++i) {
+            acc0 += red[i][0][lane];
+            acc1 += red[i][1][lane];
         }
     }
     bf16x8 o;
@@ -122,8 +143,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
                              void* out, float* lse, hipStream_t stream) {
     if (pairs == 0) return SMLA_OK;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)pairs), dim3(64), 0, stream, part_out, part_lse, num_splits,
-                       pairs, (uint16_t*)out, lse);
+    // few pairs (small batch): four waves per pair so that more part loads are in flight
+    if (pairs <= 512)
+        hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)pairs), dim3(256), 0, stream, part_out, part_lse,
+                           num_splits, pairs, (uint16_t*)out, lse);
+    else
+        hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)pairs), dim3(64), 0, stream, part_out, part_lse,
+                           num_splits, pairs, (uint16_t*)out, lse);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 

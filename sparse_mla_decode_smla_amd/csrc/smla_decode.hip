@@ -164,22 +164,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
     const int ntiles = (nk + kTile - 1) / kTile;
 
-    // ---- logical positions -> physical rows (masked entries -> -1), all waves
+    // ---- logical positions -> physical rows (masked entries -> -1), all waves.
+    // When the sequence's block-table row is short, it is first copied into the
+    // (still empty) stage ring together with the index list, so each entry
+    // costs one LDS lookup instead of a second dependent global load.
     {
         int64_t cap = (int64_t)kBlock * a.max_blocks;
         if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
         const int32_t* idx = a.indices + (int64_t)r * a.topk + k0;
         const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
-        for (int i = tid; i < ntiles * kTile; i += kThreads) {
-            int row = -1;
-            if (i < nk) {
-                const int pos = idx[i];
+        const int nent = ntiles * kTile;
+        constexpr int kMaxBtInLds = 4096;
+        static_assert(kMaxBtInLds * 4 <= NST * STAGE, "block-table copy exceeds the stage ring");
+        if (a.max_blocks <= kMaxBtInLds) {
+            __attribute__((address_space(3))) int* btl = (__attribute__((address_space(3))) int*)lds;
+            for (int i = tid; i < a.max_blocks; i += kThreads) btl[i] = bt[i];
+            for (int i = tid; i < nent; i += kThreads)
+                *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = i < nk ? idx[i] : -1;
+            __syncthreads();
+            for (int i = tid; i < nent; i += kThreads) {
+                __attribute__((address_space(3))) int* e = (__attribute__((address_space(3))) int*)(rowtab + 4 * i);
+                const int pos = *e;
+                int row = -1;
                 if (pos >= 0 && (int64_t)pos < cap) {
-                    const int blk = bt[pos / kBlock];
+                    const int blk = btl[pos / kBlock];
                     if (blk >= 0 && (int64_t)blk < a.num_kv_blocks) row = blk * kBlock + (pos % kBlock);
                 }
+                *e = row;
             }
-            *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
+        } else {
+            for (int i = tid; i < nent; i += kThreads) {
+                int row = -1;
+                if (i < nk) {
+                    const int pos = idx[i];
+                    if (pos >= 0 && (int64_t)pos < cap) {
+                        const int blk = bt[pos / kBlock];
+                        if (blk >= 0 && (int64_t)blk < a.num_kv_blocks) row = blk * kBlock + (pos % kBlock);
+                    }
+                }
+                *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
+            }
         }
     }
 
