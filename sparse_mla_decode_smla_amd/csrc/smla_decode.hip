@@ -164,11 +164,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
     const int ntiles = (nk + kTile - 1) / kTile;
 
-    // ---- logical positions -> physical rows (masked entries -> -1), all waves.
-    // When the sequence's block-table row is short, it is first copied into the
-    // (still empty) stage ring together with the index list, so each entry
-    // costs one LDS lookup instead of a second dependent global load.
-    {
+    // ---- logical positions -> physical rows (masked entries -> -1), by the PV
+    // waves (threads 256..511) while the QK waves load Q.  When the
+    // sequence's block-table row is short, it is first copied into the (still
+    // empty) stage ring together with the index list, so each entry costs one
+    // LDS lookup instead of a second dependent global load.  Barriers T1 (copy
+    // done) and B0 (row table done) are run by every wave.
+    auto build_row_table = [&]() {
+        const int pt = tid - 4 * 64;  // 0..255
         int64_t cap = (int64_t)kBlock * a.max_blocks;
         if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
         const int32_t* idx = a.indices + (int64_t)r * a.topk + k0;
@@ -178,11 +181,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         static_assert(kMaxBtInLds * 4 <= NST * STAGE, "block-table copy exceeds the stage ring");
         if (a.max_blocks <= kMaxBtInLds) {
             __attribute__((address_space(3))) int* btl = (__attribute__((address_space(3))) int*)lds;
-            for (int i = tid; i < a.max_blocks; i += kThreads) btl[i] = bt[i];
-            for (int i = tid; i < nent; i += kThreads)
+            for (int i = pt; i < a.max_blocks; i += 256) btl[i] = bt[i];
+            for (int i = pt; i < nent; i += 256)
                 *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = i < nk ? idx[i] : -1;
-            __syncthreads();
-            for (int i = tid; i < nent; i += kThreads) {
+            __syncthreads();  // T1
+            for (int i = pt; i < nent; i += 256) {
                 __attribute__((address_space(3))) int* e = (__attribute__((address_space(3))) int*)(rowtab + 4 * i);
                 const int pos = *e;
                 int row = -1;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 *e = row;
             }
         } else {
-            for (int i = tid; i < nent; i += kThreads) {
+            for (int i = pt; i < nent; i += 256) {
                 int row = -1;
                 if (i < nk) {
                     const int pos = idx[i];
@@ -204,8 +207,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
             }
+            __syncthreads();  // T1
         }
-    }
+    };
 
     // ---- output staging: the normalised output goes through the (then idle)
     // stage ring, 32 heads at a time, so that every head's row is written to
@@ -235,9 +239,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 *(bf16x4*)o = v0;
                 *(bf16x4*)(o + 256) = v1;
             } else {
+                // (streaming stores: the partials are read once, by the combine kernel)
                 float* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 4 * lane;
-                *(f32x4*)o = x0;
-                *(f32x4*)(o + 256) = x1;
+                __builtin_nontemporal_store(x0, (f32x4*)o);
+                __builtin_nontemporal_store(x1, (f32x4*)(o + 256));
             }
         }
     };
@@ -285,8 +290,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     static_assert(LPT_PV + LPT_QK == NBANDS + (FMT == 0 ? 0 : 1), "the two roles cover every band of a slice");
 
-    // Every wave runs the same sequence of workgroup barriers: B0 (row table
-    // ready), P0 (tile 0 in LDS), E_k at the end of each step k in
+    // Every wave runs the same sequence of workgroup barriers: T1 and B0 (row
+    // table ready), P0 (tile 0 in LDS), E_k at the end of each step k in
     // [0, ntiles], D (denominators), then three for the output halves.  In
     // step k the QK waves turn tile k into softmax weights P(k); the PV waves
     // add tile k-1 to the output with P(k-1) (from V held in registers) while
@@ -314,10 +319,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 qreg[kk] = *(const bf16x8*)(qh + d);
             }
         }
+        __syncthreads();  // T1
+        __syncthreads();  // B0
         wait_vmcnt<0>();
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
-        __syncthreads();  // B0
 
         // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
         // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
@@ -543,6 +549,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     } else {
         // ========= PV waves: value dims [128p, 128p + 128), all heads =========
         const int p = wave - 4;
+        build_row_table();
         __syncthreads();  // B0
 
         // V^T operand offsets: the k-slots 8g .. 8g + 7 of a lane are the tokens
