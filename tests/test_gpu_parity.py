@@ -240,6 +240,51 @@ def test_runs_on_a_side_stream():
     check(out, lse, ref_o, ref_l, "side stream")
 
 
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+def test_multi_token_verify(fmt):
+    """Four query tokens per sequence (speculative-decode verify), each with its own top-k list:
+    rows (b, s) are independent; the block table and the cache are shared by a sequence's tokens."""
+    inp = I.small_inputs(batch=3, q_len=4, topk=160, seq_len=700, kv_format=fmt, seed=90)
+    ref_o, ref_l = oracle.decode_inputs(inp)
+    for splits in (0, 1, 3):
+        out, lse = run_gpu(inp, force_splits=splits)
+        check(out, lse, ref_o, ref_l, f"q_len=4 splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_graph_capture_replays(splits):
+    """run (partial + combine) captured once in a HIP graph and replayed three times, the inputs
+    rewritten in place by eager work between replays; every replay matches the oracle."""
+    inp = I.small_inputs(batch=2, q_len=1, topk=256, seq_len=1024, kv_format=I.KV_BF16, seed=95)
+    w = inp.workload
+    q, kv, bt, idx, sl = B().to_device(inp)
+    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, force_splits=splits)
+    out = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device="cuda")
+    ws = B().alloc_workspace(plan, "cuda")
+    stream = torch.cuda.Stream()
+    B().decode_run(plan, q, kv, bt, idx, sl, inp.softmax_scale, out, lse, ws)  # warm (per-device setup)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            B().decode_run(plan, q, kv, bt, idx, sl, inp.softmax_scale, out, lse, ws, stream=stream)
+    rng = np.random.default_rng(96)
+    for rep in range(3):
+        # new index lists and query values for this replay, written in place (eager work)
+        new_idx = np.stack([rng.permutation(1024)[:256] for _ in range(2)]).astype(np.int32).reshape(2, 1, 256)
+        new_idx[1, 0, rng.choice(256, size=40, replace=False)] = -1
+        new_q = I.bf16_bits_rne(rng.standard_normal(inp.q.shape).astype(np.float32)).astype(np.uint16)
+        idx.copy_(torch.from_numpy(new_idx))
+        q.copy_(torch.from_numpy(new_q.view(np.int16)).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        inp_r = I.Inputs(**{**inp.__dict__, "q": new_q, "indices": new_idx})
+        ref_o, ref_l = oracle.decode_inputs(inp_r)
+        check(out, lse, ref_o, ref_l, f"graph replay {rep} splits={plan.num_splits}")
+
+
 # ---------------------------------------------------------------- full workloads
 
 @pytest.fixture(scope="module")
