@@ -40,16 +40,18 @@ int query_cu_count(int* out) {
 // Estimated time (us) of one call with S parts per row, from a model fitted
 // to measurements of the two kernels on MI355X (256 CUs):
 //   - a workgroup gathers its part at about 30 GB/s per CU, and the whole
-//     launch at most at about 5 TB/s; a 32-token tile costs about 0.55 us of
-//     compute (bf16 rows) or 1.7 us (fp8 rows, widened in registers); the
-//     partial kernel pays about 6 us of launch, prologue and epilogue;
-//   - with S > 1 every part writes 64 x 512 fp32 outputs (128 KiB) per row,
-//     which the combine kernel reads back: both move at about 5 TB/s, and the
-//     combine pays about 3 us plus 0.08 us per part (its load batches).
+//     launch at most at about 5 TB/s; a 32-token tile costs about 0.9 us of
+//     pipelined compute (bf16 rows) or 1.7 us (fp8 rows, widened in
+//     registers); the partial kernel pays about 6 us of launch, prologue and
+//     epilogue;
+//   - with S > 1 every part writes 64 x 512 fp32 outputs (128 KiB) per row at
+//     about 5 TB/s, which the combine kernel reads back at about 8 TB/s (they
+//     were just written); the combine pays about 2.3 us plus 0.25 us per round
+//     of 16 part loads.
 // Workgroups beyond one per CU run in further rounds.
 double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus) {
     const double row_bytes = p.kv_format == SMLA_KV_BF16 ? smla::kRowBytesBf16 : smla::kRowBytesFp8;
-    const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.55 : 1.7;
+    const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.9 : 1.7;
     const int tps = (tiles + S - 1) / S;
     const double wgs = (double)rows * S;
     const double rounds = std::ceil(wgs / cus);
@@ -59,7 +61,7 @@ double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus)
     const double t_compute = t_tile * tps * rounds;
     const double partial = S > 1 ? wgs * smla::kHeads * smla::kDv * 4.0 : 0.0;
     double t = 6.0 + std::max(t_gather, t_compute) + partial / 5e6;
-    if (S > 1) t += 3.0 + partial / 5e6 + 0.08 * S;
+    if (S > 1) t += 2.3 + partial / 8e6 + 0.25 * std::ceil(S / 16.0);
     return t;
 }
 
