@@ -612,17 +612,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         };
 
-        // step k: `cur` holds tile k-1's slice, `nxt` receives tile k's
-        auto step = [&](int k, VSlice& cur, VSlice& nxt) {
-            // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
+        // step k: `cur` holds tile k-1's slice, `nxt` receives tile k's; `gt` is
+        // the prepared refill of this step (tile k + NST - 1 into the stage of
+        // tile k - 1, free since E_{k-1}), `gt_next` receives the next step's.
+        // LDS reads are ordered so that the MFMAs wait only for P: the flags
+        // and P first, then the copy of tile k's V slice.
+        auto step = [&](int k, VSlice& cur, VSlice& nxt, const Gather& gt, Gather& gt_next) {
             const bool refill = k + NST - 1 < ntiles;
-            Gather gt;
-            if (refill) gt = prepare(k + NST - 1);
-            if (k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);
+            const int kp = (k - 1) & 1;
+            i32x4 fl = i32x4{0, 0, 0, 0};
+            bf16x8 pbh[4];
             if (k >= 1) {
-                const int kp = (k - 1) & 1;
+                fl = lds_load<i32x4>(aux + AUX_FLAG + 16 * kp);
+                const lds_u8* pr = p_read + kp * PBUF;
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(pr + hb * 1024);
                 // heads whose reference was raised at tile k-1: rescale their accumulators first
-                const i32x4 fl = lds_load<i32x4>(aux + AUX_FLAG + 16 * kp);
                 if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb)
@@ -632,12 +637,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                             for (int db = 0; db < 8; ++db) oacc[db][hb] *= al;
                         }
                 }
+            }
+            if (k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);
+            if (k >= 1) {
                 // ---- O^T[this wave's 128 dims, all heads] += V^T . P^T over tile k-1,
                 // with the refill DMAs between its MFMAs
-                const lds_u8* pr = p_read + kp * PBUF;
-                bf16x8 pbh[4];
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(pr + hb * 1024);
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
                     // (bf16: the bf16-typed transpose read; rebuilding the operand element
@@ -656,6 +660,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
             }
+            if (k + NST < ntiles) gt_next = prepare(k + NST);
             if (k + 1 < ntiles) wait_tiles<LPT_PV>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
         };
@@ -666,15 +671,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
         }
+        Gather ga, gb;
+        if (NST - 1 < ntiles) ga = prepare(NST - 1);
         if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
         __syncthreads();  // P0
         VSlice v0, v1;
         int k = 0;
         for (; k + 1 <= ntiles; k += 2) {
-            step(k, v1, v0);
-            step(k + 1, v0, v1);
+            step(k, v1, v0, ga, gb);
+            step(k + 1, v0, v1, gb, ga);
         }
-        if (k <= ntiles) step(k, v1, v0);
+        if (k <= ntiles) step(k, v1, v0, ga, gb);
         __syncthreads();  // D
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
