@@ -7,7 +7,8 @@ argument marshalling around the C functions, plus ``build()`` which compiles
 
 Functions (see ``oracle.c`` for the definitions and the passages they follow):
 
-* ``bf16_to_f64``, ``e4m3fn_to_f64`` -- exact decoding of the input formats;
+* ``bf16_to_f64``, ``e4m3fn_to_f64``, ``ue8m0_to_f64`` -- exact decoding of
+  the input formats;
 * ``sparse_mla_decode`` -- out/lse of sparse softmax attention per head;
 * ``lse_combine`` -- merge of partial (out, lse) pairs over parts of a list.
 
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 KV_BF16 = 0
 KV_FP8 = 1
+KV_FP8_NOPE_UE8M0 = 2
 
 
 def build(force: bool = True, src: str = SOURCE, out_path: str = LIB_PATH) -> str:
@@ -50,8 +52,12 @@ def _bind(path: str):
     lib.oracle_bf16_array_to_f64.restype = None
     lib.oracle_e4m3fn_array_to_f64.argtypes = [i64, P, P]
     lib.oracle_e4m3fn_array_to_f64.restype = None
+    lib.oracle_ue8m0_array_to_f64.argtypes = [i64, P, P]
+    lib.oracle_ue8m0_array_to_f64.restype = None
     lib.oracle_row_bytes.argtypes = [i32, i32, i32]
     lib.oracle_row_bytes.restype = i64
+    lib.oracle_block_bytes.argtypes = [i32, i32, i32, i32]
+    lib.oracle_block_bytes.restype = i64
     lib.oracle_sparse_mla_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i64, i32,
                                              P, P, P, P, P, f64, P, P, i32]
     lib.oracle_sparse_mla_decode.restype = ctypes.c_int
@@ -83,16 +89,25 @@ class Oracle:
         self.lib.oracle_e4m3fn_array_to_f64(codes.size, _ptr(codes), _ptr(out))
         return out
 
+    def ue8m0_to_f64(self, codes: np.ndarray) -> np.ndarray:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape, dtype=np.float64)
+        self.lib.oracle_ue8m0_array_to_f64(codes.size, _ptr(codes), _ptr(out))
+        return out
+
     def row_bytes(self, kv_format: int, d_qk: int, d_v: int) -> int:
         return int(self.lib.oracle_row_bytes(kv_format, d_qk, d_v))
+
+    def block_bytes(self, kv_format: int, block_size: int, d_qk: int, d_v: int) -> int:
+        return int(self.lib.oracle_block_bytes(kv_format, block_size, d_qk, d_v))
 
     def sparse_mla_decode(self, q_bits, kv_cache, block_table, indices, seq_lens, softmax_scale, *,
                           d_v: int, kv_format: int, block_size: int, threads: int = 1):
         """fp64 (out [B, q_len, H, d_v], lse [B, q_len, H]).
 
         q_bits: uint16 [B, q_len, H, d_qk] (bf16 bit patterns); kv_cache: uint8
-        [num_blocks, block_size, row_bytes]; block_table: int32 [B, max_blocks];
-        indices: int32 [B, q_len, topk]; seq_lens: int32 [B] or None.
+        [num_blocks, ...] with block_bytes per block; block_table: int32 [B,
+        max_blocks]; indices: int32 [B, q_len, topk]; seq_lens: int32 [B] or None.
         """
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
         B, q_len, H, d_qk = q_bits.shape
@@ -103,10 +118,10 @@ class Oracle:
             raise ValueError(f"indices shape {indices.shape} does not match q {q_bits.shape}")
         if block_table.ndim != 2 or block_table.shape[0] != B:
             raise ValueError(f"block_table shape {block_table.shape} does not match batch {B}")
-        rb = self.row_bytes(kv_format, d_qk, d_v)
-        if kv_cache.ndim != 3 or kv_cache.shape[1] != block_size or kv_cache.shape[2] != rb:
-            raise ValueError(f"kv_cache shape {kv_cache.shape} does not match block_size {block_size}, "
-                             f"row bytes {rb}")
+        bb = self.block_bytes(kv_format, block_size, d_qk, d_v)
+        if bb < 0 or kv_cache.ndim < 2 or kv_cache[0].size != bb:
+            raise ValueError(f"kv_cache shape {kv_cache.shape} does not match {bb} bytes per block "
+                             f"(format {kv_format}, block_size {block_size})")
         if seq_lens is not None:
             seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
             if seq_lens.shape != (B,):
@@ -169,8 +184,16 @@ def e4m3fn_to_f64(codes):
     return default().e4m3fn_to_f64(codes)
 
 
+def ue8m0_to_f64(codes):
+    return default().ue8m0_to_f64(codes)
+
+
 def row_bytes(kv_format, d_qk, d_v):
     return default().row_bytes(kv_format, d_qk, d_v)
+
+
+def block_bytes(kv_format, block_size, d_qk, d_v):
+    return default().block_bytes(kv_format, block_size, d_qk, d_v)
 
 
 def sparse_mla_decode(*args, **kwargs):

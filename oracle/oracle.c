@@ -14,7 +14,9 @@
  *       lse     = m + ln Z                         (natural log)
  *       out[d]  = sum_j exp(score_j - m) * V_{L_j}[d] / Z,   d < d_v
  *   K is the whole latent row of a token (the c_kv part followed by the rope
- *   part) and V is the c_kv part of the same row.
+ *   part) and V is its first d_v values: the c_kv part for kv_formats 0 and
+ *   1 (d_v < d_qk), the whole row, rope included, for kv_format 2
+ *   (d_v = d_qk).
  *   Sources:
  *   - "The MMA Sparse-MLA Decode Kernel: A Deep Dive into AI Inference
  *     Optimization on Blackwell GPUs", Agent Reasoning, "Kernel Structure
@@ -41,12 +43,23 @@
  *   - the list is a multiset: a repeated index counts once per occurrence;
  *   - a row with no valid index yields out = 0 and lse = -inf.
  *
- * Byte layout of one token row (row_bytes per token, rows of a block are
- * contiguous, blocks are contiguous):
- *   kv_format 0 (bf16):  d_qk bf16 values, 2*d_qk bytes.
- *   kv_format 1 (fp8):   d_v  OCP e4m3fn bytes (the c_kv part), then
- *                        (d_qk-d_v) bf16 rope values, then d_v/128 fp32
- *                        scales; c_kv element d is e4m3(byte d) * scale[d/128].
+ * Byte layout of the cache (blocks of block_size tokens are contiguous):
+ *   kv_format 0 (bf16):  a block is block_size token rows of d_qk bf16
+ *                        values, 2*d_qk bytes each.
+ *   kv_format 1 (fp8):   a block is block_size token rows of d_v OCP e4m3fn
+ *                        bytes (the c_kv part), then (d_qk-d_v) bf16 rope
+ *                        values, then d_v/128 fp32 scales; c_kv element d is
+ *                        e4m3(byte d) * scale[d/128].
+ *   kv_format 2 (the pages' paged layout, "Cache Layout Understanding" and
+ *                "Kernel Structure Analysis"): d_qk = d_v = 512.  A token's
+ *                latent row is 448 "nope" values stored as OCP e4m3fn bytes
+ *                followed by 64 rope values stored as bf16 (576 bytes); the
+ *                nope values carry one UE8M0 scale per group of 64 (7 scale
+ *                bytes, padded to 8).  A block holds the 576-byte rows of all
+ *                its tokens first, then the 8-byte scale records of all its
+ *                tokens (584 bytes per token slot).  Element d < 448 of the
+ *                row is e4m3(byte d) * ue8m0(scale byte d/64); the values V
+ *                are the whole 512-wide row, rope included.
  */
 #include <math.h>
 #include <pthread.h>
@@ -91,6 +104,13 @@ double oracle_e4m3fn_to_f64(uint8_t x)
     return sign ? -v : v;
 }
 
+/* UE8M0 (the OCP microscaling scale format): 8 exponent bits, no sign, no
+ * mantissa; code e is 2^(e-127) and code 255 is NaN. */
+double oracle_ue8m0_to_f64(uint8_t e)
+{
+    return e == 0xff ? NAN : ldexp(1.0, (int)e - 127);
+}
+
 /* IEEE binary32 stored little-endian. */
 static double f32_le_to_f64(const uint8_t *p)
 {
@@ -120,23 +140,55 @@ void oracle_e4m3fn_array_to_f64(int64_t n, const uint8_t *in, double *out)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3fn_to_f64(in[i]);
 }
 
+void oracle_ue8m0_array_to_f64(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_ue8m0_to_f64(in[i]);
+}
+
+/* kv_format 2: widths of the pages' layout. */
+#define V4_NOPE 448          /* e4m3fn values per token */
+#define V4_ROPE 64           /* bf16 values per token */
+#define V4_GROUP 64          /* nope values per scale */
+#define V4_DATA_BYTES (V4_NOPE + 2 * V4_ROPE)   /* 576 */
+#define V4_SCALE_BYTES 8     /* 7 scales + 1 pad byte */
+
+/* Bytes per token slot (for kv_format 2: row plus scale record); -1 if the
+ * format does not fit the widths. */
 int64_t oracle_row_bytes(int32_t kv_format, int32_t d_qk, int32_t d_v)
 {
     if (kv_format == 0) return 2 * (int64_t)d_qk;
     if (kv_format == 1) return (int64_t)d_v + 2 * (int64_t)(d_qk - d_v) + 4 * (int64_t)(d_v / 128);
+    if (kv_format == 2) return (d_qk == V4_NOPE + V4_ROPE && d_v == d_qk) ? V4_DATA_BYTES + V4_SCALE_BYTES : -1;
     return -1;
 }
 
-/* Decode one token row into K[0..d_qk). */
-static void decode_token_row(int32_t kv_format, int32_t d_qk, int32_t d_v, const uint8_t *row, double *k)
+/* Bytes of one cache block of block_size tokens. */
+int64_t oracle_block_bytes(int32_t kv_format, int32_t block_size, int32_t d_qk, int32_t d_v)
+{
+    int64_t rb = oracle_row_bytes(kv_format, d_qk, d_v);
+    return rb < 0 ? -1 : rb * block_size;
+}
+
+/* Decode the token in slot `slot` of the block at `block` into K[0..d_qk). */
+static void decode_token(int32_t kv_format, int32_t d_qk, int32_t d_v, int32_t block_size, const uint8_t *block,
+                         int slot, double *k)
 {
     if (kv_format == 0) {
+        const uint8_t *row = block + (int64_t)slot * oracle_row_bytes(0, d_qk, d_v);
         for (int d = 0; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(row + 2 * d));
-    } else {
+    } else if (kv_format == 1) {
+        const uint8_t *row = block + (int64_t)slot * oracle_row_bytes(1, d_qk, d_v);
         const uint8_t *rope = row + d_v;
         const uint8_t *scales = row + d_v + 2 * (d_qk - d_v);
         for (int d = 0; d < d_v; ++d) k[d] = oracle_e4m3fn_to_f64(row[d]) * f32_le_to_f64(scales + 4 * (d / 128));
         for (int d = d_v; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(rope + 2 * (d - d_v)));
+    } else {
+        const uint8_t *row = block + (int64_t)slot * V4_DATA_BYTES;
+        const uint8_t *scales = block + (int64_t)block_size * V4_DATA_BYTES + (int64_t)slot * V4_SCALE_BYTES;
+        for (int d = 0; d < V4_NOPE; ++d)
+            k[d] = oracle_e4m3fn_to_f64(row[d]) * oracle_ue8m0_to_f64(scales[d / V4_GROUP]);
+        for (int d = V4_NOPE; d < d_qk; ++d)
+            k[d] = oracle_bf16_to_f64(load_u16_le(row + V4_NOPE + 2 * (d - V4_NOPE)));
     }
 }
 
@@ -171,7 +223,7 @@ static void decode_one_row(decode_job *J, int64_t r, double *kbuf, double *score
 {
     const int H = J->num_heads, DQK = J->d_qk, DV = J->d_v;
     const int b = (int)(r / J->q_len);
-    const int64_t row_bytes = oracle_row_bytes(J->kv_format, DQK, DV);
+    const int64_t block_bytes = oracle_block_bytes(J->kv_format, J->block_size, DQK, DV);
     const int32_t *idx = J->indices + r * J->topk;
 
     /* Valid list L, decoded once and shared by all heads. */
@@ -179,7 +231,8 @@ static void decode_one_row(decode_job *J, int64_t r, double *kbuf, double *score
     for (int j = 0; j < J->topk; ++j) {
         int64_t pr = physical_row(J, b, idx[j]);
         if (pr < 0) continue;
-        decode_token_row(J->kv_format, DQK, DV, J->kv_cache + pr * row_bytes, kbuf + (int64_t)n * DQK);
+        decode_token(J->kv_format, DQK, DV, J->block_size, J->kv_cache + (pr / J->block_size) * block_bytes,
+                     (int)(pr % J->block_size), kbuf + (int64_t)n * DQK);
         ++n;
     }
 
@@ -242,7 +295,7 @@ static void *decode_worker(void *arg)
 
 /*
  * q:           bf16 [batch, q_len, num_heads, d_qk]
- * kv_cache:    bytes [num_kv_blocks, block_size, row_bytes]
+ * kv_cache:    bytes [num_kv_blocks, block_bytes] (layout above)
  * block_table: int32 [batch, max_blocks_per_seq]
  * indices:     int32 [batch, q_len, topk]
  * seq_lens:    int32 [batch] or NULL
@@ -261,8 +314,9 @@ int oracle_sparse_mla_decode(int32_t batch, int32_t q_len, int32_t num_heads, in
     if (batch < 0 || q_len <= 0 || num_heads <= 0 || d_v <= 0 || d_qk < d_v || topk < 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_kv_blocks < 0)
         return ORACLE_BAD_ARG;
-    if (kv_format != 0 && kv_format != 1) return ORACLE_BAD_ARG;
+    if (kv_format != 0 && kv_format != 1 && kv_format != 2) return ORACLE_BAD_ARG;
     if (kv_format == 1 && d_v % 128 != 0) return ORACLE_BAD_ARG;
+    if (oracle_row_bytes(kv_format, d_qk, d_v) < 0) return ORACLE_BAD_ARG;
     if ((int64_t)batch * q_len == 0) return ORACLE_OK;
     if (!q || !kv_cache || !block_table || !indices || !out || !lse) return ORACLE_BAD_ARG;
 

@@ -24,7 +24,14 @@ Recipe (seed 0 unless given; numpy PCG64 streams from ``SeedSequence(seed).spawn
 * fp8 cache rows: c_kv quantised per group of 128 values with fp32 scale
   amax/448 to OCP e4m3fn (round to nearest even, via torch), rope in bf16,
   row bytes = [512 e4m3][64 bf16 rope][4 fp32 scales] = 656 bytes;
-* softmax scale: fp32(1/sqrt(576)).
+* the pages' paged layout (kv_format 2, "Cache Layout Understanding"): 448
+  nope values per token drawn as N(0, 1) * 2^u with u uniform in {-3..0} per
+  group of 64 (so the groups' scales differ), quantised per group with the
+  power-of-two scale 2^e, e = ceil(log2(amax / 448)), to OCP e4m3fn (round to
+  nearest even), e stored as the UE8M0 byte e + 127; 64 rope values N(0, 1)
+  in bf16.  A 64-token block is the 64 token rows [448 e4m3][64 bf16] (576
+  bytes each) followed by the 64 scale records [7 UE8M0][1 zero pad byte];
+* softmax scale: fp32(1/sqrt(d_qk)) (576, or 512 for kv_format 2).
 
 Large caches are filled only at the rows some index selects ("selected"
 fill); the other rows stay zero.  Small caches are filled completely.
@@ -39,6 +46,14 @@ import numpy as np
 
 KV_BF16 = 0
 KV_FP8 = 1
+KV_FP8_NOPE_UE8M0 = 2
+
+# kv_format 2 widths
+V4_NOPE = 448
+V4_ROPE = 64
+V4_GROUP = 64
+V4_DATA_BYTES = V4_NOPE + 2 * V4_ROPE   # 576
+V4_SCALE_BYTES = 8
 
 FILL_ALL_MAX_BYTES = 256 << 20
 
@@ -68,7 +83,12 @@ class Workload:
 
     @property
     def row_bytes(self) -> int:
+        """Bytes per token slot (for kv_format 2: the row plus its scale record)."""
         return kv_row_bytes(self.kv_format, self.d_qk, self.d_v)
+
+    @property
+    def block_bytes(self) -> int:
+        return self.block_size * self.row_bytes
 
 
 def kv_row_bytes(kv_format: int, d_qk: int = 576, d_v: int = 512) -> int:
@@ -76,6 +96,10 @@ def kv_row_bytes(kv_format: int, d_qk: int = 576, d_v: int = 512) -> int:
         return 2 * d_qk
     if kv_format == KV_FP8:
         return d_v + 2 * (d_qk - d_v) + 4 * (d_v // 128)
+    if kv_format == KV_FP8_NOPE_UE8M0:
+        if d_qk != V4_NOPE + V4_ROPE or d_v != d_qk:
+            raise ValueError("kv_format 2 has d_qk = d_v = 512")
+        return V4_DATA_BYTES + V4_SCALE_BYTES
     raise ValueError(f"unknown kv_format {kv_format}")
 
 
@@ -90,6 +114,12 @@ WORKLOADS = [
              paged=True, seq_len_range=(1024, 131072)),
     Workload("b128_q2_topk2048_n65536_paged_fp8", batch=128, q_len=2, topk=2048, kv_format=KV_FP8,
              paged=True, seq_len=65536),
+    # the pages' own cache layout and decode step: top-512 selection, contexts
+    # up to 8192 tokens, batch 1 and the batch-64 serving point
+    Workload("b1_topk512_n8192_paged_v4fp8", batch=1, q_len=1, topk=512, kv_format=KV_FP8_NOPE_UE8M0,
+             paged=True, seq_len=8192, d_qk=512, d_v=512),
+    Workload("b64_topk512_n8192_paged_v4fp8", batch=64, q_len=1, topk=512, kv_format=KV_FP8_NOPE_UE8M0,
+             paged=True, seq_len=8192, d_qk=512, d_v=512),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -98,7 +128,7 @@ WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
 class Inputs:
     workload: Workload
     q: np.ndarray             # uint16 [B, q_len, H, d_qk] bf16 bits
-    kv_cache: np.ndarray      # uint8 [num_blocks, block_size, row_bytes]
+    kv_cache: np.ndarray      # uint8 [num_blocks, block_size, row_bytes]; kv_format 2: [num_blocks, block_bytes]
     block_table: np.ndarray   # int32 [B, max_blocks]
     indices: np.ndarray       # int32 [B, q_len, topk]
     seq_lens: np.ndarray      # int32 [B]
@@ -135,11 +165,25 @@ def _e4m3fn_codes(x: np.ndarray) -> np.ndarray:
 
 
 def encode_rows(w: Workload, values: np.ndarray) -> np.ndarray:
-    """Cache bytes uint8 [n, row_bytes] of float32 latent rows [n, d_qk] in the workload's format."""
+    """Cache bytes uint8 [n, row_bytes] of float32 latent rows [n, d_qk] in the workload's format.
+
+    For kv_format 2 a returned row is the token's 576-byte row followed by its
+    8-byte scale record; the two go to different places of the block."""
     values = np.ascontiguousarray(values, dtype=np.float32)
     n = values.shape[0]
     if w.kv_format == KV_BF16:
         return bf16_bits_rne(values).view(np.uint8).reshape(n, w.row_bytes)
+    if w.kv_format == KV_FP8_NOPE_UE8M0:
+        groups = values[:, :V4_NOPE].reshape(n, V4_NOPE // V4_GROUP, V4_GROUP)
+        amax = np.abs(groups).max(axis=2).astype(np.float64)
+        e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / 448.0)), 0.0)
+        e = np.clip(e, -126, 127).astype(np.int32)
+        codes = _e4m3fn_codes(groups / np.ldexp(1.0, e)[:, :, None].astype(np.float32))
+        out = np.zeros((n, w.row_bytes), dtype=np.uint8)
+        out[:, :V4_NOPE] = codes.reshape(n, V4_NOPE)
+        out[:, V4_NOPE:V4_DATA_BYTES] = bf16_bits_rne(values[:, V4_NOPE:]).view(np.uint8).reshape(n, -1)
+        out[:, V4_DATA_BYTES:V4_DATA_BYTES + V4_NOPE // V4_GROUP] = (e + 127).astype(np.uint8)
+        return out
     c = values[:, : w.d_v]
     rope = bf16_bits_rne(values[:, w.d_v:])
     groups = c.reshape(n, w.d_v // 128, 128)
@@ -157,6 +201,12 @@ def _row_values(w: Workload, rng: np.random.Generator, n: int) -> np.ndarray:
     """Bytes of n token rows, uint8 [n, row_bytes]."""
     if w.kv_format == KV_BF16:
         return encode_rows(w, rng.standard_normal((n, w.d_qk), dtype=np.float32))
+    if w.kv_format == KV_FP8_NOPE_UE8M0:
+        nope = rng.standard_normal((n, V4_NOPE // V4_GROUP, V4_GROUP), dtype=np.float32)
+        u = rng.integers(-3, 1, size=(n, V4_NOPE // V4_GROUP, 1))
+        nope = (nope * np.ldexp(1.0, u)).astype(np.float32).reshape(n, V4_NOPE)
+        rope = rng.standard_normal((n, V4_ROPE), dtype=np.float32)
+        return encode_rows(w, np.concatenate([nope, rope], axis=1))
     c = rng.standard_normal((n, w.d_v), dtype=np.float32)
     rope = rng.standard_normal((n, w.d_qk - w.d_v), dtype=np.float32)
     return encode_rows(w, np.concatenate([c, rope], axis=1))
@@ -204,7 +254,8 @@ def make_inputs(w: Workload, seed: int = 0, fill: Optional[str] = None, index_se
     cache_bytes = total_blocks * bs * rb
     if fill is None:
         fill = "all" if cache_bytes <= FILL_ALL_MAX_BYTES else "selected"
-    kv = np.zeros((total_blocks, bs, rb), dtype=np.uint8)
+    kv = np.zeros((total_blocks, bs, rb) if w.kv_format != KV_FP8_NOPE_UE8M0 else (total_blocks, bs * rb),
+                  dtype=np.uint8)
     if fill == "all":
         rows = np.arange(total_blocks * bs, dtype=np.int64)
     elif fill == "selected":
@@ -217,11 +268,20 @@ def make_inputs(w: Workload, seed: int = 0, fill: Optional[str] = None, index_se
         rows = np.unique(np.concatenate(sel)) if sel else np.zeros(0, np.int64)
     else:
         raise ValueError(f"fill must be 'all' or 'selected', not {fill!r}")
-    flat = kv.reshape(-1, rb)
     chunk = 1 << 18
-    for start in range(0, rows.size, chunk):
-        part = rows[start: start + chunk]
-        flat[part] = _row_values(w, r_kv, part.size)
+    if w.kv_format == KV_FP8_NOPE_UE8M0:
+        data = kv[:, : bs * V4_DATA_BYTES].reshape(total_blocks, bs, V4_DATA_BYTES)
+        recs = kv[:, bs * V4_DATA_BYTES:].reshape(total_blocks, bs, V4_SCALE_BYTES)
+        for start in range(0, rows.size, chunk):
+            part = rows[start: start + chunk]
+            vals = _row_values(w, r_kv, part.size)
+            data[part // bs, part % bs] = vals[:, :V4_DATA_BYTES]
+            recs[part // bs, part % bs] = vals[:, V4_DATA_BYTES:]
+    else:
+        flat = kv.reshape(-1, rb)
+        for start in range(0, rows.size, chunk):
+            part = rows[start: start + chunk]
+            flat[part] = _row_values(w, r_kv, part.size)
 
     scale = float(np.float32(1.0 / math.sqrt(w.d_qk)))
     return Inputs(workload=w, q=q, kv_cache=kv, block_table=block_table, indices=indices,
@@ -232,8 +292,10 @@ def make_inputs(w: Workload, seed: int = 0, fill: Optional[str] = None, index_se
 def small_inputs(batch=2, q_len=1, topk=96, seq_len=256, kv_format=KV_BF16, paged=True, seed=0,
                  num_heads=64, seq_len_range=None) -> Inputs:
     """A small workload of the same structure, for tests that the oracle runs in seconds."""
-    w = Workload(f"small_b{batch}_q{q_len}_topk{topk}_n{seq_len}_{'fp8' if kv_format else 'bf16'}",
+    fmt_name = {KV_BF16: "bf16", KV_FP8: "fp8", KV_FP8_NOPE_UE8M0: "v4fp8"}[kv_format]
+    d_qk = 512 if kv_format == KV_FP8_NOPE_UE8M0 else 576
+    w = Workload(f"small_b{batch}_q{q_len}_topk{topk}_n{seq_len}_{fmt_name}",
                  batch=batch, q_len=q_len, topk=topk, kv_format=kv_format, paged=paged,
                  seq_len=None if seq_len_range else seq_len, seq_len_range=seq_len_range,
-                 num_heads=num_heads)
+                 num_heads=num_heads, d_qk=d_qk, d_v=512)
     return make_inputs(w, seed=seed, fill="all")

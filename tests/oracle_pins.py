@@ -11,7 +11,11 @@ the oracle disagrees with:
   paged cache, masking by -1 / out-of-range entries;
 * closed forms: a single selected token, a zero query, identical rows,
   repeated indices, and the combine's own special cases;
-* library conversions (torch) of every bf16 and e4m3fn bit pattern.
+* library conversions (torch) of every bf16, e4m3fn and UE8M0 bit pattern.
+
+kv_format 2 (the pages' paged layout: per block, the 576-byte token rows,
+then the 8-byte scale records) is decoded here with numpy slicing of the
+block and torch's float8_e4m3fn / float8_e8m0fnu conversions.
 
 The same battery is run against deliberately broken copies of the oracle
 source to show that plausible mistakes are caught.
@@ -38,12 +42,27 @@ def np_e4m3(codes: np.ndarray) -> np.ndarray:
     return t.to(torch.float64).numpy()
 
 
+def np_ue8m0(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e8m0fnu)
+    return t.to(torch.float64).numpy()
+
+
 def token_rows(inp: I.Inputs, b: int, positions: np.ndarray) -> np.ndarray:
     """Decoded latent rows K [n, d_qk] (float64) of logical positions of sequence b."""
     w = inp.workload
     bs, rb = w.block_size, w.row_bytes
-    flat = inp.kv_cache.reshape(-1, rb)
     positions = np.asarray(positions, dtype=np.int64)
+    if w.kv_format == I.KV_FP8_NOPE_UE8M0:
+        nb = inp.kv_cache.shape[0]
+        blocks = inp.kv_cache.reshape(nb, -1)
+        blk = inp.block_table[b, positions // bs].astype(np.int64)
+        slot = positions % bs
+        data = blocks[:, : bs * 576].reshape(nb, bs, 576)[blk, slot]       # [n, 576]
+        rec = blocks[:, bs * 576:].reshape(nb, bs, 8)[blk, slot]           # [n, 8]
+        nope = np_e4m3(data[:, :448]) * np.repeat(np_ue8m0(rec[:, :7]), 64, axis=1)
+        rope = np_bf16(np.ascontiguousarray(data[:, 448:]).view(np.uint16))
+        return np.concatenate([nope, rope], axis=1)
+    flat = inp.kv_cache.reshape(-1, rb)
     phys = inp.block_table[b, positions // bs].astype(np.int64) * bs + positions % bs
     raw = flat[phys]
     if w.kv_format == I.KV_BF16:
@@ -106,6 +125,15 @@ def pin_e4m3_table(orc):
     assert np.array_equal(got[~nan], ref[~nan]), "e4m3fn decode differs from torch"
 
 
+def pin_ue8m0_table(orc):
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    ref = np_ue8m0(codes)
+    got = orc.ue8m0_to_f64(codes)
+    assert np.isnan(ref[255]) and np.isnan(ref).sum() == 1, "torch should report code 255 as the only NaN"
+    assert np.isnan(got[255]) and not np.isnan(got[:255]).any(), "UE8M0 NaN code differs"
+    assert np.array_equal(got[:255], ref[:255]), "UE8M0 decode differs from torch"
+
+
 # ----------------------------------------------------------------- dense brute force
 
 
@@ -128,6 +156,11 @@ def pin_dense_bf16(orc):
 
 def pin_dense_fp8(orc):
     _dense_pin(orc, I.small_inputs(batch=2, q_len=2, topk=256, seq_len=256, kv_format=I.KV_FP8, seed=2))
+
+
+def pin_dense_v4(orc):
+    _dense_pin(orc, I.small_inputs(batch=2, q_len=2, topk=256, seq_len=256, kv_format=I.KV_FP8_NOPE_UE8M0,
+                                   seed=15))
 
 
 def pin_dense_ragged_padded(orc):
@@ -173,7 +206,15 @@ def pin_split_combine(orc):
 
 
 def pin_paging(orc):
-    inp = I.small_inputs(batch=3, q_len=1, topk=100, seq_len=320, kv_format=I.KV_FP8, seed=6)
+    _paging_pin(orc, I.small_inputs(batch=3, q_len=1, topk=100, seq_len=320, kv_format=I.KV_FP8, seed=6))
+
+
+def pin_paging_v4(orc):
+    _paging_pin(orc, I.small_inputs(batch=3, q_len=1, topk=100, seq_len=320, kv_format=I.KV_FP8_NOPE_UE8M0,
+                                    seed=16))
+
+
+def _paging_pin(orc, inp):
     out, lse = orc.decode_inputs(inp)
     w = inp.workload
     bs = w.block_size
@@ -270,6 +311,19 @@ def pin_single_token(orc):
             assert_close(lse[b, s], ref_l, 1e-12, "one token: lse = scaled score")
 
 
+def pin_single_token_v4(orc):
+    inp = I.small_inputs(batch=1, q_len=2, topk=40, seq_len=256, kv_format=I.KV_FP8_NOPE_UE8M0, seed=17)
+    idx = np.full_like(inp.indices, -1)
+    idx[0, 0, 5] = 200
+    idx[0, 1, 39] = 3
+    out, lse = orc.decode_inputs(inp, indices=idx)
+    for s, p in ((0, 200), (1, 3)):
+        K = token_rows(inp, 0, np.array([p]))[0]
+        assert np.array_equal(out[0, s], np.broadcast_to(K, out[0, s].shape)), \
+            "one token: out must equal its whole row (rope included) exactly"
+        assert_close(lse[0, s], (np_bf16(inp.q[0, s]) @ K) * inp.softmax_scale, 1e-12, "one token: lse")
+
+
 def pin_zero_query(orc):
     inp = I.small_inputs(batch=1, q_len=1, topk=77, seq_len=256, kv_format=I.KV_BF16, seed=11)
     q0 = np.zeros_like(inp.q)
@@ -296,6 +350,25 @@ def pin_identical_rows(orc):
     assert_close(out[0, 0], np.broadcast_to(K[: w.d_v], out[0, 0].shape), 1e-13, "identical rows: out = V")
     s = (np_bf16(inp.q[0, 0]) @ K) * inp.softmax_scale
     assert_close(lse[0, 0], s + math.log(90), 1e-12, "identical rows: lse = s + ln n")
+
+
+def pin_identical_rows_v4(orc):
+    inp = I.small_inputs(batch=1, q_len=1, topk=70, seq_len=192, kv_format=I.KV_FP8_NOPE_UE8M0, seed=18)
+    nb = inp.kv_cache.shape[0]
+    kv = inp.kv_cache.copy()
+    data = kv[:, : 64 * 576].reshape(nb, 64, 576)
+    rec = kv[:, 64 * 576:].reshape(nb, 64, 8)
+    data[:] = data[1, 7].copy()                          # every token row and scale record identical
+    rec[:] = rec[1, 7].copy()
+    w = inp.workload
+    out, lse = orc.sparse_mla_decode(inp.q, kv, inp.block_table, inp.indices, inp.seq_lens,
+                                     inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format,
+                                     block_size=w.block_size)
+    inp2 = I.Inputs(**{**inp.__dict__, "kv_cache": kv})
+    K = token_rows(inp2, 0, np.array([0]))[0]
+    assert_close(out[0, 0], np.broadcast_to(K, out[0, 0].shape), 1e-13, "identical rows: out = V")
+    s = (np_bf16(inp.q[0, 0]) @ K) * inp.softmax_scale
+    assert_close(lse[0, 0], s + math.log(70), 1e-12, "identical rows: lse = s + ln n")
 
 
 def pin_duplicates(orc):
@@ -333,7 +406,8 @@ def pin_combine_closed_forms(orc):
 
 
 ALL_PINS = [
-    pin_bf16_table, pin_e4m3_table, pin_dense_bf16, pin_dense_fp8, pin_dense_ragged_padded,
-    pin_permutation, pin_split_combine, pin_paging, pin_masking, pin_seq_lens_mask, pin_empty_row,
-    pin_single_token, pin_zero_query, pin_identical_rows, pin_duplicates, pin_combine_closed_forms,
+    pin_bf16_table, pin_e4m3_table, pin_ue8m0_table, pin_dense_bf16, pin_dense_fp8, pin_dense_v4,
+    pin_dense_ragged_padded, pin_permutation, pin_split_combine, pin_paging, pin_paging_v4, pin_masking,
+    pin_seq_lens_mask, pin_empty_row, pin_single_token, pin_single_token_v4, pin_zero_query,
+    pin_identical_rows, pin_identical_rows_v4, pin_duplicates, pin_combine_closed_forms,
 ]

@@ -76,3 +76,37 @@ def test_selected_fill_covers_every_selected_row():
             p = idx[b].reshape(-1).astype(np.int64)
             phys = inp.block_table[b, p // bs].astype(np.int64) * bs + p % bs
             assert np.all(rows[phys, 640:656].view(np.float32) > 0), "a selected row was left unfilled"
+
+
+def test_v4_block_layout_and_quantisation():
+    # kv_format 2: per block, 64 rows of [448 e4m3][64 bf16] then 64 records of [7 UE8M0][pad]
+    inp = I.small_inputs(batch=2, topk=64, seq_len=256, kv_format=I.KV_FP8_NOPE_UE8M0, seed=3)
+    nb = inp.kv_cache.shape[0]
+    assert inp.kv_cache.shape == (nb, 64 * 584)
+    data = inp.kv_cache[:, : 64 * 576].reshape(-1, 576)
+    rec = inp.kv_cache[:, 64 * 576:].reshape(-1, 8)
+    assert np.all(rec[:, 7] == 0), "pad byte must be zero"
+    e = rec[:, :7].astype(np.int64) - 127
+    assert e.min() >= -126 and e.max() <= 127
+    assert len(np.unique(e)) >= 3, "group scales should differ"
+    codes = torch.from_numpy(np.ascontiguousarray(data[:, :448])).view(torch.float8_e4m3fn).to(torch.float64)
+    codes = codes.numpy().reshape(-1, 7, 64)
+    assert not np.isnan(codes).any()
+    amax = np.abs(codes).max(axis=2)
+    # a power-of-two scale leaves each group's largest magnitude in (224, 448]
+    assert np.all(amax <= 448.0) and np.all(amax > 224.0 * (1 - 2 ** -4))
+    rope = np.ascontiguousarray(data[:, 448:]).view(np.uint16)
+    assert rope.shape[1] == 64 and np.isfinite(
+        torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).float().numpy()).all()
+    assert abs(inp.softmax_scale - 1 / np.sqrt(512)) < 1e-7
+
+
+def test_v4_selected_fill():
+    w = I.WORKLOADS_BY_NAME["b1_topk512_n8192_paged_v4fp8"]
+    inp = I.make_inputs(w, fill="selected")
+    bs = w.block_size
+    nb = inp.kv_cache.shape[0]
+    rec = inp.kv_cache[:, bs * 576:].reshape(nb, bs, 8)
+    p = inp.indices[0, 0].astype(np.int64)
+    blk = inp.block_table[0, p // bs]
+    assert np.all(rec[blk, p % bs, :7] > 0), "a selected token's scale record was left unfilled"

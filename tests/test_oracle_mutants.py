@@ -53,6 +53,24 @@ MUTATIONS = [
     ("bf16 row elements swapped pairwise",
      "for (int d = 0; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(row + 2 * d));",
      "for (int d = 0; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(row + 2 * (d ^ 1)));"),
+    ("UE8M0 exponent bias off by one",
+     "return e == 0xff ? NAN : ldexp(1.0, (int)e - 127);",
+     "return e == 0xff ? NAN : ldexp(1.0, (int)e - 126);"),
+    ("UE8M0 scale group of 128 instead of 64",
+     "k[d] = oracle_e4m3fn_to_f64(row[d]) * oracle_ue8m0_to_f64(scales[d / V4_GROUP]);",
+     "k[d] = oracle_e4m3fn_to_f64(row[d]) * oracle_ue8m0_to_f64(scales[d / 128]);"),
+    ("scale record taken from the token row instead of the block's record area",
+     "const uint8_t *scales = block + (int64_t)block_size * V4_DATA_BYTES + (int64_t)slot * V4_SCALE_BYTES;",
+     "const uint8_t *scales = row + 2 * V4_NOPE / 2 + 2;"),
+    ("scale records packed at 7 bytes",
+     "const uint8_t *scales = block + (int64_t)block_size * V4_DATA_BYTES + (int64_t)slot * V4_SCALE_BYTES;",
+     "const uint8_t *scales = block + (int64_t)block_size * V4_DATA_BYTES + (int64_t)slot * 7;"),
+    ("rope read from the start of the row",
+     "k[d] = oracle_bf16_to_f64(load_u16_le(row + V4_NOPE + 2 * (d - V4_NOPE)));",
+     "k[d] = oracle_bf16_to_f64(load_u16_le(row + 2 * (d - V4_NOPE)));"),
+    ("token rows strided by the 584-byte slot",
+     "const uint8_t *row = block + (int64_t)slot * V4_DATA_BYTES;",
+     "const uint8_t *row = block + (int64_t)slot * (V4_DATA_BYTES + V4_SCALE_BYTES);"),
     ("seq_lens ignored",
      "if (J->seq_lens && (int64_t)J->seq_lens[b] < cap) cap = J->seq_lens[b];",
      ""),
