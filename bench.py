@@ -200,7 +200,7 @@ def main() -> int:
     inp = I.make_inputs(w, seed=0)
     gathered = inp.valid_count() * w.row_bytes
     q, kv, bt, idx, sl = B.to_device(inp, device=dev)
-    plan = B.decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format,
+    plan = B.decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, d_qk=w.d_qk,
                          force_splits=args.force_splits)
     out = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
@@ -286,7 +286,8 @@ def main() -> int:
         log("[bench] timing the oracle on the host")
         cpu = cpu_baseline(inp, gathered, args.cpu_seconds)
 
-    fmt_name = "bf16" if w.kv_format == I.KV_BF16 else "fp8e4m3+bf16"
+    fmt_name = {I.KV_BF16: "bf16", I.KV_FP8: "fp8e4m3+bf16",
+                I.KV_FP8_NOPE_UE8M0: "fp8e4m3(ue8m0/64)+bf16 rope, 584 B/token pages"}[w.kv_format]
     line = {
         "metric": METRIC,
         "value": round(gbs, 3),

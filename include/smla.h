@@ -67,11 +67,22 @@ typedef enum {
     /* fp8 latent rows: d_v OCP e4m3fn bytes (c_kv), then (d_qk-d_v) bf16
      * k_rope values, then d_v/128 little-endian fp32 scales; c_kv element d
      * is e4m3(byte d) * scale[d/128].  656 bytes for d_qk=576, d_v=512. */
-    SMLA_KV_FP8_E4M3_SCALE128 = 1
+    SMLA_KV_FP8_E4M3_SCALE128 = 1,
+    /* The paged layout of "The MMA Sparse-MLA Decode Kernel: A Deep Dive into
+     * AI Inference Optimization on Blackwell GPUs" (Agent Reasoning, "Cache
+     * Layout Understanding", "Kernel Structure Analysis"): d_qk = d_v = 512.
+     * A token's row is 448 "nope" values as OCP e4m3fn bytes, then 64 rope
+     * values as bf16 (576 bytes); a block of 64 tokens is its 64 rows, then
+     * 64 scale records of 8 bytes: 7 UE8M0 exponents (scale 2^(e-127) of nope
+     * values 64g .. 64g+63) and a pad byte; 37376 bytes per block (584 per
+     * token).  K = V = the whole 512-wide row: the output carries the rope
+     * part too.  Supported scale codes: 1..254. */
+    SMLA_KV_FP8_NOPE_UE8M0 = 2
 } smla_kv_format_t;
 
-/* Problem description (host).  Supported: num_heads = 64, d_qk = 576,
- * d_v = 512, block_size = 64; any batch >= 0, q_len >= 1, topk >= 0. */
+/* Problem description (host).  Supported: num_heads = 64, d_v = 512,
+ * block_size = 64, d_qk = 576 (kv_format 0, 1) or 512 (kv_format 2); any
+ * batch >= 0, q_len >= 1, topk >= 0. */
 typedef struct {
     int32_t batch;               /* B: sequences */
     int32_t q_len;               /* query tokens per sequence, each with its own top-k list */
@@ -112,7 +123,7 @@ smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out
 /*
  * Sparse MLA decode.  Shapes (R = batch * q_len, H = num_heads):
  *   q            bf16  [batch, q_len, H, d_qk]
- *   kv_cache     bytes [num_kv_blocks, block_size, row_bytes(kv_format)]
+ *   kv_cache     bytes [num_kv_blocks, block bytes of kv_format]
  *   block_table  int32 [batch, max_blocks_per_seq]: physical block of each
  *                logical block of a sequence
  *   indices      int32 [batch, q_len, topk]: logical token positions; -1 pads
@@ -121,6 +132,8 @@ smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out
  *   out          bf16  [batch, q_len, H, d_v]   (fp32 accumulation, rounded to nearest even)
  *   lse          fp32  [batch, q_len, H]        natural-log log-sum-exp of the scaled scores
  *   workspace    >= plan->workspace_bytes bytes, 256-byte aligned (may be NULL if 0)
+ * q, kv_cache and out must be 16-byte aligned, lse, block_table, indices and
+ * seq_lens 4-byte aligned (else SMLA_ERR_INVALID_ARG).
  * An index entry p of sequence b is masked (takes no part) when p < 0,
  * p >= block_size * max_blocks_per_seq, p >= seq_lens[b] (if given), or its
  * block-table entry lies outside [0, num_kv_blocks).  A row with no valid

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libsmla.so")
 
 KV_BF16 = 0
 KV_FP8_E4M3_SCALE128 = 1
+KV_FP8_NOPE_UE8M0 = 2
 
 STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED",
           3: "SMLA_ERR_WORKSPACE_TOO_SMALL", 4: "SMLA_ERR_LAUNCH", 5: "SMLA_ERR_DEVICE"}
@@ -167,7 +168,8 @@ def to_device(inp, device="cuda", indices=None):
     import torch
     w = inp.workload
     q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(device)
-    if inp.fill == "all":
+    if inp.fill == "all" or w.kv_format == KV_FP8_NOPE_UE8M0:
+        # (kv_format 2 blocks interleave rows and scale records: copied whole)
         kv = torch.from_numpy(inp.kv_cache).to(device)
     else:
         kv = torch.zeros(inp.kv_cache.shape, dtype=torch.uint8, device=device)

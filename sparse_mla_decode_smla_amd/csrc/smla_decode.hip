@@ -19,14 +19,17 @@
 //   QK^T    : S^T[token, head] = K . Q^T with v_mfma_f32_16x16x32_bf16,
 //             Q held in registers, K read from LDS (fp8 rows are widened to
 //             bf16 in registers; the per-128 fp32 scale multiplies the
-//             per-group partial scores);
+//             per-group partial scores; the power-of-two UE8M0 scales of the
+//             pages' layout are applied exactly inside the widening);
 //   softmax : online, base 2, running max and sum per head in registers,
 //             masked tokens get -inf ("Edge Case Handling": invalid tokens
 //             never enter the softmax);
 //   PV      : O^T[dim, head] += V^T . P^T with the same MFMA; V^T comes from
 //             the same LDS tile through transpose reads (ds_read_b64_tr_b16,
 //             ds_read_b64_tr_b8); fp32 accumulation, bf16 only at the store
-//             ("Design Decisions" 6).
+//             ("Design Decisions" 6).  A transposed fp8 operand holds eight
+//             tokens per lane, so per-token scales are folded into the
+//             weights P instead: one scaled copy of P per scale group.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -85,6 +88,12 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
                  "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
 }
+// 4-byte variant: lane l's 4 bytes land at lds_base + 4*l.
+__device__ __forceinline__ void lds_dma4(const void* src, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int N>
@@ -98,6 +107,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // bf16 transpose reads of 4 tokens per 16-lane group, and 8-byte fp8
 // transpose reads of tokens {4g..4g+3, 16+4g..16+4g+3} per 16-lane group g.
 __device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 4) & 1); }
+
+// Swizzle of the four 16-byte chunks of a 64-byte half-band row (v4 rows):
+// the 16-byte QK reads of 16 consecutive tokens then cover all banks.
+__device__ __forceinline__ int swz4(int t) { return (t >> 2) & 3; }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -120,6 +133,26 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(unsigned lo, unsigned hi) {
     return r;
 }
 
+// Eight e4m3fn codes times the power of two `scale` -> eight bf16 (exact
+// while the products are normal bf16 numbers).
+__device__ __forceinline__ bf16x8 e4m3x8_scaled_to_bf16(unsigned lo, unsigned hi, float scale) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// UE8M0 exponent byte `sel` (0..7) of an 8-byte scale record -> 2^(e-127)
+// as fp32 (codes 1..254; code 0 gives +0).
+__device__ __forceinline__ float ue8m0_scale(i32x2 rec, int sel) {
+    const unsigned w = (unsigned)rec[sel >> 2];
+    return __builtin_bit_cast(float, ((w >> (8 * (sel & 3))) & 0xffu) << 23);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_tiles(int after) {
     // wait until at most `after` tiles of N DMA instructions each are still in flight
@@ -135,11 +168,14 @@ __device__ __forceinline__ void wait_tiles(int after) {
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void partial_kernel(PartialArgs a) {
-    constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : kStageBytesFp8;
-    constexpr int NST = FMT == 0 ? kStagesBf16 : kStagesFp8;
-    constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : kRowBytesFp8;
-    constexpr int NBANDS = FMT == 0 ? kBandsBf16 : kBandsFp8;
+    constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : FMT == 1 ? kStageBytesFp8 : kStageBytesV4;
+    constexpr int NST = FMT == 0 ? kStagesBf16 : FMT == 1 ? kStagesFp8 : kStagesV4;
+    constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : FMT == 1 ? kRowBytesFp8 : kRowBytesV4;
+    constexpr int NBANDS = FMT == 0 ? kBandsBf16 : FMT == 1 ? kBandsFp8 : kBandsV4;
+    constexpr int DQK = FMT == 2 ? kDqkV4 : kDqk;
     constexpr int PBUF = aux_p_buffer_bytes(FMT);
+    constexpr int HALF_OFF = kBandsV4 * kTile * 128;  // v4: half band [token][64 B]
+    constexpr int REC_OFF = HALF_OFF + kTile * 64;    // v4: scale records [token][8 B]
     static_assert(NST >= 2 && NST - 2 <= 4, "stage ring depth outside what the waits cover");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_generic[];
@@ -255,15 +291,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // waves instead; measured, that was not faster.)  A tile's DMAs are
     // prepared (row-table read, addresses) first and issued one at a time, so
     // they can be spread between MFMAs.
-    constexpr int LPT_PV = FMT == 0 ? 9 : 6;
+    //   v4 rows: 4 full bands, the half band (lanes 0..31: 8 tokens x 4
+    //   chunks) and the scale records (lanes 0..15: 8 tokens x 2 dwords).
+    constexpr int DMAS_PER_SLICE = FMT == 0 ? 9 : 6;
+    constexpr int LPT_PV = DMAS_PER_SLICE;
     constexpr int LPT_QK = 0;
     const int oct = wave & 3;
     const int band0 = wave < 4 ? LPT_PV : 0;  // first band of this wave
     struct Gather {
         const unsigned char* src;   // this lane's 16 bytes of band 0 (or the zero chunk)
-        const unsigned char* src2;  // fp8: this lane's scale bytes
+        const unsigned char* src2;  // fp8: this lane's scale bytes; v4: its half-band chunk
+        const unsigned char* src3;  // v4: this lane's 4 bytes of a scale record
         int bstride;                // 128, or 0 for a masked token
         unsigned sbase;             // LDS byte address of the stage
+    };
+    // start of the row of a physical token (v4: rows and scale records are
+    // separate areas of a block)
+    auto row_base = [&](int row) -> const unsigned char* {
+        if (FMT == 2) return a.kv + (int64_t)(row >> 6) * kBlockBytesV4 + (row & 63) * kRowBytesV4;
+        return a.kv + (int64_t)row * ROWB;
     };
     auto prepare = [&](int tile) {
         Gather gt;
@@ -271,13 +317,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int t = 8 * oct + (lane >> 3);  // token of this lane within the tile
         const int row = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t));
         const int chunk = (lane & 7) ^ swz(t);
-        gt.src = row >= 0 ? a.kv + (int64_t)row * ROWB + chunk * 16 : kZeroChunk;
+        gt.src = row >= 0 ? row_base(row) + chunk * 16 : kZeroChunk;
         gt.bstride = row >= 0 ? 128 : 0;
         gt.src2 = kZeroChunk;
+        gt.src3 = kZeroChunk;
         if (FMT == 1) {
             const int t2 = 8 * oct + (lane & 7);
             const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
             gt.src2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
+        }
+        if (FMT == 2) {
+            const int th = 8 * oct + ((lane >> 2) & 7);
+            const int rowh = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + th));
+            gt.src2 = rowh >= 0 ? row_base(rowh) + 4 * 128 + (((lane & 3) ^ swz4(th)) << 4) : kZeroChunk;
+            const int ts = 8 * oct + ((lane >> 1) & 7);
+            const int rows = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + ts));
+            gt.src3 = rows >= 0 ? a.kv + (int64_t)(rows >> 6) * kBlockBytesV4 + kBlock * kRowBytesV4 +
+                                      (rows & 63) * kScaleRecBytesV4 + 4 * (lane & 1)
+                                : kZeroChunk;
         }
         return gt;
     };
@@ -285,10 +342,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int bd = band0 + i;
         if (bd < NBANDS)
             lds_dma16(gt.src + bd * gt.bstride, gt.sbase + (unsigned)((bd * kTile + 8 * oct) * 128));
-        else if (lane < 8)
-            lds_dma16(gt.src2, gt.sbase + (unsigned)(NBANDS * kTile * 128 + 8 * oct * 16));
+        else if (FMT == 1) {
+            if (lane < 8) lds_dma16(gt.src2, gt.sbase + (unsigned)(NBANDS * kTile * 128 + 8 * oct * 16));
+        } else if (bd == NBANDS) {
+            if (lane < 32) lds_dma16(gt.src2, gt.sbase + (unsigned)(HALF_OFF + 8 * oct * 64));
+        } else {
+            if (lane < 16) lds_dma4(gt.src3, gt.sbase + (unsigned)(REC_OFF + 8 * oct * kScaleRecBytesV4));
+        }
     };
-    static_assert(LPT_PV + LPT_QK == NBANDS + (FMT == 0 ? 0 : 1), "the two roles cover every band of a slice");
+    static_assert(LPT_PV + LPT_QK == DMAS_PER_SLICE, "the two roles cover every DMA of a slice");
 
     // Every wave runs the same sequence of workgroup barriers: T1 and B0 (row
     // table ready), P0 (tile 0 in LDS), E_k at the end of each step k in
@@ -306,13 +368,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // lane); for fp8 rows the c_kv dims of k-steps 2p and 2p+1 inside a
         // 128-group are the two halves of one 16-byte run, so one LDS read
         // feeds two k-steps.
-        bf16x8 qreg[18];
+        // (v4 rows: the 16-byte run of nope group u feeds k-steps 2u and 2u+1;
+        // k-steps 14 and 15 are the rope values.)
+        constexpr int NQ = FMT == 2 ? 16 : 18;
+        bf16x8 qreg[NQ];
         {
-            const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * kDqk;
+            const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * DQK;
 #pragma unroll
-            for (int kk = 0; kk < 18; ++kk) {
+            for (int kk = 0; kk < NQ; ++kk) {
                 int d;
-                if (FMT == 0 || kk >= 16)
+                if (FMT == 2)
+                    d = kk < 14 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : kNopeV4 + 32 * (kk - 14) + 8 * g;
+                else if (FMT == 0 || kk >= 16)
                     d = 32 * kk + 8 * g;
                 else
                     d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
@@ -323,7 +390,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();  // B0
         wait_vmcnt<0>();
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
+        for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
 
         // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
         // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
@@ -335,6 +402,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz(tokA0)) << 4);
             qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz(tokA1)) << 4);
         }
+        // v4: this lane's chunk of the half band (rope values 32 + 8g .. 32 + 8g + 7)
+        const int qh0 = HALF_OFF + tokA0 * 64 + ((g ^ swz4(tokA0)) << 4);
+        const int qh1 = HALF_OFF + tokA1 * 64 + ((g ^ swz4(tokA1)) << 4);
         // P slot of this lane: (block q, group g, lane i16): its 8 weights are
         // the k-slots 8g .. 8g + 7 of the PV B operand, i.e. tokens
         // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
@@ -403,6 +473,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+                } else if (FMT == 2) {
+                    // 9 load units per block: nope groups 0..6 (16 e4m3 values of this
+                    // lane's token, two k-steps, widened with the token's scale of
+                    // that group), then rope values 0..31 and 32..63 (bf16)
+                    constexpr int PF = 3;
+                    u32x4 ka[PF], kb[PF];
+                    auto unit_off = [&](int u, int blk) {
+                        const int* qo = blk == 0 ? qk0 : qk1;
+                        return u < 8 ? qo[u & 1] + (u >> 1) * kTile * 128 : (blk == 0 ? qh0 : qh1);
+                    };
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
+                        kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
+                    }
+                    const i32x2 ra = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA0);
+                    const i32x2 rb = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA1);
+#pragma unroll
+                    for (int u = 0; u < 9; ++u) {
+                        const int sl = u % PF;
+                        if (u < 7) {
+                            const float fa = ue8m0_scale(ra, u), fb = ue8m0_scale(rb, u);
+                            s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][0], ka[sl][1], fa), qreg[2 * u], s0);
+                            s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][0], kb[sl][1], fb), qreg[2 * u], s1);
+                            s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][2], ka[sl][3], fa), qreg[2 * u + 1], s0);
+                            s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][2], kb[sl][3], fb), qreg[2 * u + 1], s1);
+                        } else {
+                            s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[7 + u], s0);
+                            s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[7 + u], s1);
+                        }
+                        if (u + PF < 9) {
+                            ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
+                            kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
+                        }
+                    }
                 } else {
                     // 10 load units per block: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
                     constexpr int PF = 3;
@@ -509,6 +614,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pf[e];
                     *(__attribute__((address_space(3))) bf16x8*)pbuf = pb;
+                } else if (FMT == 2) {
+                    // copies 0..6: the weights times each token's scale of nope group c;
+                    // copy 7 (rope values): the weights
+                    const lds_u8* rec = lds + (k % NST) * STAGE + REC_OFF;
+                    const i32x4 c0a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0);
+                    const i32x4 c0b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0 + 16);
+                    const i32x4 c1a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1);
+                    const i32x4 c1b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1 + 16);
+                    const i32x2 rc[8] = {i32x2{c0a[0], c0a[1]}, i32x2{c0a[2], c0a[3]}, i32x2{c0b[0], c0b[1]},
+                                         i32x2{c0b[2], c0b[3]}, i32x2{c1a[0], c1a[1]}, i32x2{c1a[2], c1a[3]},
+                                         i32x2{c1b[0], c1b[1]}, i32x2{c1b[2], c1b[3]}};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        bf16x8 pg;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pg[e] = (__bf16)(c < 7 ? pf[e] * ue8m0_scale(rc[e], c) : pf[e]);
+                        *(__attribute__((address_space(3))) bf16x8*)(pbuf + c * kPBytesPerCopy) = pg;
+                    }
                 } else {
 #pragma unroll
                     for (int grp = 0; grp < 4; ++grp) {
@@ -558,6 +681,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         //         at 4(i16 & 3) of 16-dim block m; the transpose read hands lane i dim i.
         //   fp8 : band p (the scale group), 16-dim block c; lane i16 addresses token
         //         slot j = i16 >> 1, 8 dims at 8(i16 & 1).
+        //   v4  : as fp8 (band p = nope groups 2p, 2p+1); wave 7 (p = 3) has nope
+        //         group 6 in blocks 0..3 and the bf16 rope values in blocks 4..7
+        //         (band 3 bytes 64..127, then the half band), read as for bf16.
         int pv[8];
         if (FMT == 0) {
 #pragma unroll
@@ -574,7 +700,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int c = 0; c < 8; ++c) pv[c] = (p * kTile + ta) * 128 + ((c ^ swz(ta)) << 4) + 8 * (i16 & 1);
         }
-        const lds_u8* const p_read = aux + (FMT == 0 ? 0 : p * kPBytesPerCopy) + lane * 16;  // + hb * 1024 + buffer
+        // P copies of this wave: fp8 rows copy p; v4 rows copies 2p (blocks 0..3) and 2p+1 (blocks 4..7)
+        const lds_u8* const p_read = aux + (FMT == 0 ? 0 : FMT == 1 ? p : 2 * p) * kPBytesPerCopy + lane * 16;
+        const bool rope_wave = FMT == 2 && p == 3;  // v4: blocks 4..7 are bf16 rope values
 
         f32x4 oacc[8][4];  // O^T [16-dim block of this wave's 128 dims][16-head block]
 #pragma unroll
@@ -589,12 +717,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // of that step although the product runs one step later.  Two register
         // buffers alternate: a step first copies tile k (the QK waves' MFMAs
         // run meanwhile), then multiplies tile k-1 (overlapping the QK waves'
-        // softmax).
+        // softmax).  v4 rows hold twice the P operands, and there one buffer
+        // is used: the step multiplies tile k-1, then copies tile k.
+        constexpr bool DBUF = FMT != 2;
         //   bf16: va/vb[db] = transpose reads of 16-dim block db, tokens of block 0 / 1
         //   fp8 : vr[db] = 8-bit transpose read of 16-dim block db
+        //   v4  : as fp8; in the rope wave, rope block j = db - 4 is held as
+        //         vr[db] (tokens of block 0, bit-cast) and vx[j] (block 1)
         struct VSlice {
             bf16x4 va[8], vb[8];
             i32x2 vr[8];
+            bf16x4 vx[4];
+        };
+        // v4 rope block j (values 16j .. 16j + 15), token block blk: transpose-read address
+        auto rope_off = [&](int j, int blk) {
+            const int ta = 16 * blk + 4 * g + (i16 >> 2);
+            const int x = (i16 & 3) >> 1;
+            if (j < 2) return (3 * kTile + ta) * 128 + (((2 * (2 + j) + x) ^ swz(ta)) << 4) + 8 * (i16 & 1);
+            return HALF_OFF + ta * 64 + (((2 * (j - 2) + x) ^ swz4(ta)) << 4) + 8 * (i16 & 1);
         };
         auto load_v = [&](VSlice& v, const lds_u8* st) {
             if (FMT == 0) {
@@ -604,6 +744,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         (__attribute__((address_space(3))) bf16x4*)(st + pv[db & 3] + (db >> 2) * kTile * 128));
                     v.vb[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4*)(st + pv[4 + (db & 3)] + (db >> 2) * kTile * 128));
+                }
+            } else if (FMT == 2 && rope_wave) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    v.vr[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(st + pv[db]));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v.vr[4 + j] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4*)(st + rope_off(j, 0))));
+                    v.vx[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4*)(st + rope_off(j, 1)));
                 }
             } else {
 #pragma unroll
@@ -621,12 +772,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const bool refill = k + NST - 1 < ntiles;
             const int kp = (k - 1) & 1;
             i32x4 fl = i32x4{0, 0, 0, 0};
-            bf16x8 pbh[4];
+            constexpr int NPB = FMT == 2 ? 8 : 4;  // P operands: [copy][16-head block]
+            bf16x8 pbh[NPB];
             if (k >= 1) {
                 fl = lds_load<i32x4>(aux + AUX_FLAG + 16 * kp);
                 const lds_u8* pr = p_read + kp * PBUF;
 #pragma unroll
-                for (int hb = 0; hb < 4; ++hb) pbh[hb] = lds_load<bf16x8>(pr + hb * 1024);
+                for (int i = 0; i < NPB; ++i) pbh[i] = lds_load<bf16x8>(pr + (i >> 2) * kPBytesPerCopy + (i & 3) * 1024);
                 // heads whose reference was raised at tile k-1: rescale their accumulators first
                 if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
@@ -638,7 +790,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         }
                 }
             }
-            if (k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);
+            if (DBUF && k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);
             if (k >= 1) {
                 // ---- O^T[this wave's 128 dims, all heads] += V^T . P^T over tile k-1,
                 // with the refill DMAs between its MFMAs
@@ -646,10 +798,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int db = 0; db < 8; ++db) {
                     // (bf16: the bf16-typed transpose read; rebuilding the operand element
                     // by element from the i16-typed form is miscompiled)
-                    const bf16x8 av = FMT == 0 ? __builtin_shufflevector(cur.va[db], cur.vb[db], 0, 1, 2, 3, 4, 5, 6, 7)
-                                               : e4m3x8_to_bf16((unsigned)cur.vr[db][0], (unsigned)cur.vr[db][1]);
+                    bf16x8 av;
+                    if (FMT == 0)
+                        av = __builtin_shufflevector(cur.va[db], cur.vb[db], 0, 1, 2, 3, 4, 5, 6, 7);
+                    else if (FMT == 2 && db >= 4 && rope_wave)
+                        av = __builtin_shufflevector(__builtin_bit_cast(bf16x4, cur.vr[db]), cur.vx[db - 4], 0, 1, 2, 3,
+                                                     4, 5, 6, 7);
+                    else
+                        av = e4m3x8_to_bf16((unsigned)cur.vr[db][0], (unsigned)cur.vr[db][1]);
+                    const int pc = FMT == 2 ? 4 * (db >> 2) : 0;  // P copy of this block
 #pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[hb], oacc[db][hb]);
+                    for (int hb = 0; hb < 4; ++hb) oacc[db][hb] = mfma16(av, pbh[pc + hb], oacc[db][hb]);
                     if (refill && db < LPT_PV) issue_one(gt, db);
                 }
                 if (refill) {
@@ -660,6 +819,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
             }
+            if (!DBUF && k < ntiles) load_v(nxt, lds + (k % NST) * STAGE);  // (nxt is cur)
             if (k + NST < ntiles) gt_next = prepare(k + NST);
             if (k + 1 < ntiles) wait_tiles<LPT_PV>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
@@ -676,12 +836,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
         __syncthreads();  // P0
         VSlice v0, v1;
+        VSlice& w1 = DBUF ? v1 : v0;
         int k = 0;
         for (; k + 1 <= ntiles; k += 2) {
-            step(k, v1, v0, ga, gb);
-            step(k + 1, v0, v1, gb, ga);
+            step(k, w1, v0, ga, gb);
+            step(k + 1, v0, w1, gb, ga);
         }
-        if (k <= ntiles) step(k, v1, v0, ga, gb);
+        if (k <= ntiles) step(k, w1, v0, ga, gb);
         __syncthreads();  // D
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -746,6 +907,10 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
     if (plan->rows == 0) return SMLA_OK;
     if (!q || !block_table || !out || !lse) return SMLA_ERR_INVALID_ARG;
     if (!indices && plan->prob.topk > 0) return SMLA_ERR_INVALID_ARG;
+    // alignment of the kernels' vector accesses
+    if (((uintptr_t)q & 15) || ((uintptr_t)kv_cache & 15) || ((uintptr_t)out & 15) || ((uintptr_t)lse & 3) ||
+        ((uintptr_t)block_table & 3) || ((uintptr_t)indices & 3) || ((uintptr_t)seq_lens & 3))
+        return SMLA_ERR_INVALID_ARG;
     if (num_kv_blocks < 0 || (num_kv_blocks > 0 && !kv_cache)) return SMLA_ERR_INVALID_ARG;
     if (num_kv_blocks > (int64_t)(INT32_MAX / kBlock)) return SMLA_ERR_UNSUPPORTED;
     if (!std::isfinite(softmax_scale)) return SMLA_ERR_INVALID_ARG;
@@ -777,8 +942,12 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
 
     const size_t lds = partial_lds_bytes(plan->prob.kv_format, plan->tokens_per_split);
     (void)hipGetLastError();  // clear an earlier, unrelated error
-    hipError_t e = plan->prob.kv_format == SMLA_KV_BF16 ? launch_partial<0>(args, plan->num_workgroups, lds, stream)
-                                                        : launch_partial<1>(args, plan->num_workgroups, lds, stream);
+    hipError_t e;
+    switch (plan->prob.kv_format) {
+        case SMLA_KV_BF16: e = launch_partial<0>(args, plan->num_workgroups, lds, stream); break;
+        case SMLA_KV_FP8_E4M3_SCALE128: e = launch_partial<1>(args, plan->num_workgroups, lds, stream); break;
+        default: e = launch_partial<2>(args, plan->num_workgroups, lds, stream); break;
+    }
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 

@@ -42,16 +42,16 @@ int query_cu_count(int* out) {
 //   - a workgroup gathers its part at about 30 GB/s per CU, and the whole
 //     launch at most at about 5 TB/s; a 32-token tile costs about 0.9 us of
 //     pipelined compute (bf16 rows) or 1.7 us (fp8 rows, widened in
-//     registers); the partial kernel pays about 6 us of launch, prologue and
-//     epilogue;
+//     registers; v4 rows 1.4 us); the partial kernel pays about 6 us of
+//     launch, prologue and epilogue;
 //   - with S > 1 every part writes 64 x 512 fp32 outputs (128 KiB) per row at
 //     about 5 TB/s, which the combine kernel reads back at about 8 TB/s (they
 //     were just written); the combine pays about 2.3 us plus 0.25 us per round
 //     of 16 part loads.
 // Workgroups beyond one per CU run in further rounds.
 double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus) {
-    const double row_bytes = p.kv_format == SMLA_KV_BF16 ? smla::kRowBytesBf16 : smla::kRowBytesFp8;
-    const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.9 : 1.7;
+    const double row_bytes = smla::gathered_bytes_per_token(p.kv_format);
+    const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.9 : p.kv_format == SMLA_KV_FP8_E4M3_SCALE128 ? 1.7 : 1.4;
     const int tps = (tiles + S - 1) / S;
     const double wgs = (double)rows * S;
     const double rounds = std::ceil(wgs / cus);
@@ -89,9 +89,12 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
     if (p.batch < 0 || p.q_len < 1 || p.topk < 0 || p.max_blocks_per_seq < 1 || p.num_cus < 0 ||
         p.force_splits < 0 || p.reserved != 0)
         return SMLA_ERR_INVALID_ARG;
-    if (p.num_heads != kHeads || p.d_qk != kDqk || p.d_v != kDv || p.block_size != kBlock)
+    if (p.kv_format != SMLA_KV_BF16 && p.kv_format != SMLA_KV_FP8_E4M3_SCALE128 &&
+        p.kv_format != SMLA_KV_FP8_NOPE_UE8M0)
         return SMLA_ERR_UNSUPPORTED;
-    if (p.kv_format != SMLA_KV_BF16 && p.kv_format != SMLA_KV_FP8_E4M3_SCALE128) return SMLA_ERR_UNSUPPORTED;
+    const int want_dqk = p.kv_format == SMLA_KV_FP8_NOPE_UE8M0 ? kDqkV4 : kDqk;
+    if (p.num_heads != kHeads || p.d_qk != want_dqk || p.d_v != kDv || p.block_size != kBlock)
+        return SMLA_ERR_UNSUPPORTED;
     const int64_t rows64 = (int64_t)p.batch * p.q_len;
     if (rows64 > (1 << 24)) return SMLA_ERR_UNSUPPORTED;
     if ((int64_t)p.max_blocks_per_seq * kBlock > INT32_MAX) return SMLA_ERR_UNSUPPORTED;

@@ -57,13 +57,14 @@ def test_status_strings():
 # split counts the plan's cost model chooses for the workloads on 256 CUs
 PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_paged_bf16": 32,
                   "b16_topk2048_n65536_paged_bf16": 11, "b64_topk2048_n1k-128k_paged_bf16": 3,
-                  "b128_q2_topk2048_n65536_paged_fp8": 1}
+                  "b128_q2_topk2048_n65536_paged_fp8": 1, "b1_topk512_n8192_paged_v4fp8": 16,
+                  "b64_topk512_n8192_paged_v4fp8": 4}
 
 
 @pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
 def test_plan_covers_the_list(w):
     mb = (w.max_seq_len + 63) // 64
-    p = B.decode_plan(w.batch, w.q_len, w.topk, mb, w.kv_format, num_cus=256)
+    p = B.decode_plan(w.batch, w.q_len, w.topk, mb, w.kv_format, d_qk=w.d_qk, num_cus=256)
     assert p.rows == w.rows
     assert p.num_workgroups == p.rows * p.num_splits
     assert p.tokens_per_split % p.tile_tokens == 0
@@ -106,6 +107,8 @@ def test_forced_splits_and_edge_shapes():
 @pytest.mark.parametrize("kw,status", [
     (dict(num_heads=32), 2), (dict(d_qk=512), 2), (dict(d_v=448), 2), (dict(block_size=32), 2),
     (dict(kv_format=7), 2), (dict(q_len=0), 1), (dict(topk=-1), 1), (dict(max_blocks_per_seq=0), 1),
+    (dict(kv_format=2), 2),                        # the pages' layout is 512 wide
+    (dict(kv_format=2, d_qk=512, d_v=448), 2),
 ])
 def test_plan_rejects(kw, status):
     args = dict(batch=2, q_len=1, topk=64, max_blocks_per_seq=8, kv_format=0, num_cus=256)
@@ -146,6 +149,14 @@ def test_run_argument_checks_need_no_gpu(entry, monkeypatch):
     assert _run(bad) == 1                                    # edited plan
     empty = B.decode_plan(0, 1, 256, 8, num_cus=256)
     assert _run(empty, q=None, out=None) == 0                # nothing to do
+    ws = dict(ws=1 << 26, wsb=plan.workspace_bytes)
+    for name, off in (("q", 8), ("kv", 4), ("out", 8), ("lse", 2), ("bt", 2), ("idx", 1), ("sl", 2)):
+        base = {"sl": 1 << 27}.get(name, None)
+        base = base if base is not None else {"q": 1 << 20, "kv": 1 << 21, "bt": 1 << 22, "idx": 1 << 23,
+                                              "out": 1 << 24, "lse": 1 << 25}[name]
+        assert _run(plan, **{name: base + off}, **ws) == 1, f"misaligned {name} accepted"
+    v4 = B.decode_plan(2, 1, 256, 8, B.KV_FP8_NOPE_UE8M0, d_qk=512, num_cus=256)
+    assert v4.prob.kv_format == 2 and _run(v4, q=None) == 1
 
 
 def test_combine_argument_checks_need_no_gpu():

@@ -58,10 +58,11 @@ def run_gpu(inp, indices=None, force_splits=0, with_seq_lens=True, block_table=N
     return out, lse
 
 
-FORMATS = [I.KV_BF16, I.KV_FP8]
+FORMATS = [I.KV_BF16, I.KV_FP8, I.KV_FP8_NOPE_UE8M0]
+FMT_IDS = ["bf16", "fp8", "v4fp8"]
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("splits", [0, 1, 2, 7])
 def test_small_parity(fmt, splits):
     # top-k 200 = 6 full tiles of 32 + a ragged tail of 8; q_len 2; paged, shuffled blocks
@@ -72,7 +73,7 @@ def test_small_parity(fmt, splits):
     check(out, lse, ref_o, ref_l, f"fmt{fmt} S{splits}")
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_masking_edge_cases(fmt):
     inp = I.small_inputs(batch=4, q_len=2, topk=100, seq_len=600, kv_format=fmt, seed=21 + fmt)
     w = inp.workload
@@ -101,7 +102,7 @@ def test_masking_edge_cases(fmt):
         check(out, lse, ref_o, ref_l, f"masks fmt{fmt} S{splits}")
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_seq_lens_optional(fmt):
     inp = I.small_inputs(batch=2, q_len=1, topk=96, seq_len=256, kv_format=fmt, seed=31)
     sl = np.array([256, 120], dtype=np.int32)
@@ -114,7 +115,7 @@ def test_seq_lens_optional(fmt):
     check(out2, lse2, ref_o2, ref_l2, "without seq_lens")
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS[:2], ids=FMT_IDS[:2])
 def test_late_large_scores_restart(fmt):
     # A token near the end of each list gets a score far above the first tiles' max
     # (the rope part of its K row is a large multiple of head 0's rope query; its V
@@ -139,6 +140,25 @@ def test_late_large_scores_restart(fmt):
         check(out, lse, ref_o, ref_l, f"late large score S{splits}")
 
 
+def test_late_large_scores_v4():
+    # The pages' layout: V is the whole row, so a large K row would also be a large V
+    # row; instead head 0's query is set to 8 x the row of a token late in each list,
+    # which lifts that token's score 40 to 100 (log2 units) above the first tile's max
+    # with rows of ordinary size.
+    inp = I.small_inputs(batch=2, q_len=1, topk=256, seq_len=512, kv_format=I.KV_FP8_NOPE_UE8M0, seed=91)
+    q = inp.q.copy()
+    for b in range(2):
+        p = int(inp.indices[b, 0, 250])
+        kf = oracle_pins.token_rows(inp, b, np.array([p]))[0]
+        q[b, 0, 0] = I.bf16_bits_rne((8.0 * kf).astype(np.float32))
+    inp2 = I.Inputs(**{**inp.__dict__, "q": q})
+    ref_o, ref_l = oracle.decode_inputs(inp2)
+    assert ref_l[:, 0, 0].min() > 30, "the chosen token must dominate head 0"
+    for splits in (1, 2):
+        out, lse = run_gpu(inp2, force_splits=splits)
+        check(out, lse, ref_o, ref_l, f"v4 late large score S{splits}")
+
+
 @pytest.mark.parametrize("topk", [1, 31, 33, 64])
 def test_short_lists(topk):
     inp = I.small_inputs(batch=2, q_len=2, topk=topk, seq_len=300, kv_format=I.KV_BF16, seed=40 + topk)
@@ -159,7 +179,7 @@ def test_topk_zero_and_empty_batch():
     assert out.shape[0] == 0 and lse.shape[0] == 0
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_paging_invariance_bit_exact(fmt):
     inp = I.small_inputs(batch=2, q_len=1, topk=150, seq_len=512, kv_format=fmt, seed=50)
     w = inp.workload
@@ -240,7 +260,7 @@ def test_runs_on_a_side_stream():
     check(out, lse, ref_o, ref_l, "side stream")
 
 
-@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_multi_token_verify(fmt):
     """Four query tokens per sequence (speculative-decode verify), each with its own top-k list:
     rows (b, s) are independent; the block table and the cache are shared by a sequence's tokens."""
@@ -303,7 +323,7 @@ def _sample_rows(w, rng):
 def test_workload_parity_sampled_rows(w):
     note(f"workload {w.name}: generating")
     inp = I.make_inputs(w, seed=0)
-    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format)
+    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, d_qk=w.d_qk)
     note(f"workload {w.name}: plan splits={plan.num_splits} tps={plan.tokens_per_split} wgs={plan.num_workgroups}")
     out, lse = run_gpu(inp)   # automatic plan = the launch configuration the benchmark times
     rng = np.random.default_rng(1)
