@@ -10,7 +10,9 @@ Functions (see ``oracle.c`` for the definitions and the passages they follow):
 * ``bf16_to_f64``, ``e4m3fn_to_f64``, ``ue8m0_to_f64`` -- exact decoding of
   the input formats;
 * ``sparse_mla_decode`` -- out/lse of sparse softmax attention per head;
-* ``lse_combine`` -- merge of partial (out, lse) pairs over parts of a list.
+* ``lse_combine`` -- merge of partial (out, lse) pairs over parts of a list;
+* ``indexer_scores``, ``indexer_topk`` -- the top-k indexer that produces the
+  index lists (scores of every position, and the selection).
 
 ``Oracle(path)`` wraps any compiled copy of the source (the tests use this to
 show that planted mistakes are caught); the module-level functions use the
@@ -63,6 +65,10 @@ def _bind(path: str):
     lib.oracle_sparse_mla_decode.restype = ctypes.c_int
     lib.oracle_lse_combine.argtypes = [i32, i64, i32, P, P, P, P]
     lib.oracle_lse_combine.restype = ctypes.c_int
+    lib.oracle_indexer_scores.argtypes = [i32, i32, i32, i32, i32, i64, P, P, P, P, P, P]
+    lib.oracle_indexer_scores.restype = ctypes.c_int
+    lib.oracle_indexer_topk.argtypes = [i32, i32, i32, i32, i32, i64, P, P, P, P, i32, P, P]
+    lib.oracle_indexer_topk.restype = ctypes.c_int
     return lib
 
 
@@ -153,6 +159,45 @@ class Oracle:
             raise RuntimeError(f"oracle_lse_combine failed with code {rc}")
         return out, lse
 
+    def _indexer_args(self, q_idx, k_cache, block_table, seq_lens, block_size):
+        q_idx = np.ascontiguousarray(q_idx, dtype=np.uint16)
+        B, q_len, d_idx = q_idx.shape
+        k_cache = np.ascontiguousarray(k_cache, dtype=np.uint16)
+        if k_cache.ndim != 3 or k_cache.shape[1] != block_size or k_cache.shape[2] != d_idx:
+            raise ValueError(f"k_cache shape {k_cache.shape} does not match block_size {block_size}, d_idx {d_idx}")
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if block_table.ndim != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+            raise ValueError("block_table [B, max_blocks] and seq_lens [B] required")
+        return q_idx, k_cache, block_table, seq_lens, B, q_len, d_idx
+
+    def indexer_scores(self, q_idx, k_cache, block_table, seq_lens, *, block_size: int = 64):
+        """fp64 (scores, abs_sums) [B, q_len, block_size * max_blocks]; -inf / 0 where not a candidate."""
+        q_idx, k_cache, block_table, seq_lens, B, q_len, d_idx = self._indexer_args(q_idx, k_cache, block_table,
+                                                                                    seq_lens, block_size)
+        cap = block_size * block_table.shape[1]
+        sc = np.empty((B, q_len, cap), dtype=np.float64)
+        ab = np.empty((B, q_len, cap), dtype=np.float64)
+        rc = self.lib.oracle_indexer_scores(B, q_len, d_idx, block_size, block_table.shape[1], k_cache.shape[0],
+                                            _ptr(q_idx), _ptr(k_cache), _ptr(block_table), _ptr(seq_lens),
+                                            _ptr(sc), _ptr(ab))
+        if rc != 0:
+            raise RuntimeError(f"oracle_indexer_scores failed with code {rc}")
+        return sc, ab
+
+    def indexer_topk(self, q_idx, k_cache, block_table, seq_lens, topk: int, *, block_size: int = 64):
+        """(indices int32 [B, q_len, topk], scores fp64 [B, q_len, topk]); -1 / -inf past the candidates."""
+        q_idx, k_cache, block_table, seq_lens, B, q_len, d_idx = self._indexer_args(q_idx, k_cache, block_table,
+                                                                                    seq_lens, block_size)
+        idx = np.empty((B, q_len, topk), dtype=np.int32)
+        sc = np.empty((B, q_len, topk), dtype=np.float64)
+        rc = self.lib.oracle_indexer_topk(B, q_len, d_idx, block_size, block_table.shape[1], k_cache.shape[0],
+                                          _ptr(q_idx), _ptr(k_cache), _ptr(block_table), _ptr(seq_lens), int(topk),
+                                          _ptr(idx), _ptr(sc))
+        if rc != 0:
+            raise RuntimeError(f"oracle_indexer_topk failed with code {rc}")
+        return idx, sc
+
     def decode_inputs(self, inp, indices=None, threads: int = 1, with_seq_lens: bool = True):
         """Oracle on an ``Inputs`` object of the seeded generator."""
         w = inp.workload
@@ -206,3 +251,11 @@ def lse_combine(part_out, part_lse):
 
 def decode_inputs(inp, indices=None, threads: int = 1, with_seq_lens: bool = True):
     return default().decode_inputs(inp, indices=indices, threads=threads, with_seq_lens=with_seq_lens)
+
+
+def indexer_scores(*args, **kwargs):
+    return default().indexer_scores(*args, **kwargs)
+
+
+def indexer_topk(*args, **kwargs):
+    return default().indexer_topk(*args, **kwargs)

@@ -388,3 +388,137 @@ int oracle_lse_combine(int32_t num_splits, int64_t n, int32_t d_v, const double 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Top-k indexer: the step that produces the index lists.
+ *
+ * Sources: "The Pivot Point: When a 6.3x Kernel Speedup Reveals the Next
+ * Bottleneck", Input Knowledge Required (an indexer selects the top ~512
+ * cache positions of each decode step; the attention reads only those) and
+ * the note on the bf16 indexer product (the top-512 selection is sensitive
+ * to the precision of the scores); "The Moment of Truth: Benchmarking a
+ * Custom MMA Kernel for DeepSeek-V4-Flash on Blackwell", The Broader
+ * Context (the indexer scores every position of the context, each decode
+ * step); "The MMA Sparse-MLA Decode Kernel: A Deep Dive ...", Context (the
+ * indexer's scores come from a batched matrix product).
+ *
+ * Reading (the pages give no formula): for query row r = (b, s) the score
+ * of position p is the dot product of the row's indexer query and the
+ * indexer key of token p, both bf16 vectors of d_idx values, the keys paged
+ * with the same block table as the latent cache:
+ *     score(r, p) = sum_{d < d_idx} q_idx[r, d] * k_idx[block_table[b][p / bs], p % bs, d]
+ * over the candidate positions of sequence b: 0 <= p < min(seq_lens[b],
+ * bs * max_blocks_per_seq) whose block-table entry lies in [0, num_kv_blocks).
+ * The selection is the min(topk, #candidates) positions of highest score,
+ * ordered by score, highest first, equal scores by position, lowest first;
+ * the rest of the row's list is -1.
+ */
+
+static double indexer_score(const uint16_t *q, const uint8_t *kcache, int64_t row_bytes, int64_t phys, int32_t d_idx,
+                            double *abs_sum)
+{
+    const uint8_t *k = kcache + phys * row_bytes;
+    double acc = 0.0, a = 0.0;
+    for (int d = 0; d < d_idx; ++d) {
+        double t = oracle_bf16_to_f64(q[d]) * oracle_bf16_to_f64(load_u16_le(k + 2 * d));
+        acc += t;
+        a += fabs(t);
+    }
+    if (abs_sum) *abs_sum = a;
+    return acc;
+}
+
+/* Physical row of position p of sequence b for the indexer, or -1. */
+static int64_t indexer_phys(const int32_t *block_table, const int32_t *seq_lens, int32_t b, int32_t block_size,
+                            int32_t max_blocks, int64_t num_kv_blocks, int64_t p)
+{
+    int64_t cap = (int64_t)block_size * max_blocks;
+    if ((int64_t)seq_lens[b] < cap) cap = seq_lens[b];
+    if (p < 0 || p >= cap) return -1;
+    int32_t blk = block_table[(int64_t)b * max_blocks + p / block_size];
+    if (blk < 0 || (int64_t)blk >= num_kv_blocks) return -1;
+    return (int64_t)blk * block_size + p % block_size;
+}
+
+/*
+ * Scores of every position p < block_size * max_blocks_per_seq:
+ * scores [batch, q_len, cap] fp64 (-inf where p is not a candidate) and
+ * abs_sums [batch, q_len, cap] = sum_d |q_d * k_d| (0 where not a candidate;
+ * may be NULL).
+ * q_idx: bf16 [batch, q_len, d_idx]; k_cache: bf16 [num_kv_blocks, block_size, d_idx].
+ */
+int oracle_indexer_scores(int32_t batch, int32_t q_len, int32_t d_idx, int32_t block_size,
+                          int32_t max_blocks_per_seq, int64_t num_kv_blocks, const uint16_t *q_idx,
+                          const uint8_t *k_cache, const int32_t *block_table, const int32_t *seq_lens,
+                          double *scores, double *abs_sums)
+{
+    if (batch < 0 || q_len <= 0 || d_idx <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_kv_blocks < 0)
+        return ORACLE_BAD_ARG;
+    if ((int64_t)batch * q_len == 0) return ORACLE_OK;
+    if (!q_idx || !block_table || !seq_lens || !scores) return ORACLE_BAD_ARG;
+    if (num_kv_blocks > 0 && !k_cache) return ORACLE_BAD_ARG;
+    const int64_t cap = (int64_t)block_size * max_blocks_per_seq;
+    const int64_t row_bytes = 2 * (int64_t)d_idx;
+    for (int32_t b = 0; b < batch; ++b) {
+        for (int32_t s = 0; s < q_len; ++s) {
+            const int64_t r = (int64_t)b * q_len + s;
+            for (int64_t p = 0; p < cap; ++p) {
+                int64_t phys = indexer_phys(block_table, seq_lens, b, block_size, max_blocks_per_seq, num_kv_blocks, p);
+                double a = 0.0;
+                scores[r * cap + p] = phys < 0 ? -INFINITY
+                                               : indexer_score(q_idx + r * d_idx, k_cache, row_bytes, phys, d_idx, &a);
+                if (abs_sums) abs_sums[r * cap + p] = a;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Does (sa, pa) come before (sb, pb) in the selection order? */
+static int ranks_before(double sa, int64_t pa, double sb, int64_t pb)
+{
+    return sa > sb || (sa == sb && pa < pb);
+}
+
+/*
+ * The selection: out_idx [batch, q_len, topk] int32 positions and
+ * out_score [batch, q_len, topk] fp64 (or NULL), -1 / -inf past the
+ * candidates.  A plain selection: for each slot j the best candidate not yet
+ * taken (O(topk * cap) per row; test sizes only).
+ */
+int oracle_indexer_topk(int32_t batch, int32_t q_len, int32_t d_idx, int32_t block_size, int32_t max_blocks_per_seq,
+                        int64_t num_kv_blocks, const uint16_t *q_idx, const uint8_t *k_cache,
+                        const int32_t *block_table, const int32_t *seq_lens, int32_t topk, int32_t *out_idx,
+                        double *out_score)
+{
+    if (topk < 0) return ORACLE_BAD_ARG;
+    if ((int64_t)batch * q_len == 0 || topk == 0) return ORACLE_OK;
+    if (!out_idx) return ORACLE_BAD_ARG;
+    const int64_t cap = (int64_t)block_size * max_blocks_per_seq;
+    const int64_t rows = (int64_t)batch * q_len;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(rows * cap));
+    unsigned char *taken = (unsigned char *)malloc((size_t)cap);
+    if (!sc || !taken) {
+        free(sc); free(taken);
+        return ORACLE_NO_MEMORY;
+    }
+    int rc = oracle_indexer_scores(batch, q_len, d_idx, block_size, max_blocks_per_seq, num_kv_blocks, q_idx,
+                                   k_cache, block_table, seq_lens, sc, NULL);
+    for (int64_t r = 0; rc == ORACLE_OK && r < rows; ++r) {
+        const double *s = sc + r * cap;
+        memset(taken, 0, (size_t)cap);
+        for (int32_t j = 0; j < topk; ++j) {
+            int64_t best = -1;
+            for (int64_t p = 0; p < cap; ++p) {
+                if (taken[p] || s[p] == -INFINITY) continue;
+                if (best < 0 || ranks_before(s[p], p, s[best], best)) best = p;
+            }
+            out_idx[r * topk + j] = best < 0 ? -1 : (int32_t)best;
+            if (out_score) out_score[r * topk + j] = best < 0 ? -INFINITY : s[best];
+            if (best >= 0) taken[best] = 1;
+        }
+    }
+    free(sc);
+    free(taken);
+    return rc;
+}

@@ -299,3 +299,88 @@ def small_inputs(batch=2, q_len=1, topk=96, seq_len=256, kv_format=KV_BF16, page
                  seq_len=None if seq_len_range else seq_len, seq_len_range=seq_len_range,
                  num_heads=num_heads, d_qk=d_qk, d_v=512)
     return make_inputs(w, seed=seed, fill="all")
+
+
+# ----------------------------------------------------------------- top-k indexer inputs
+#
+# The indexer scores every position of a sequence with the dot product of the
+# row's indexer query and the token's indexer key and keeps the top-k
+# positions.  Recipe: seed 0 streams as above; q_idx and the keys are N(0, 1)
+# rounded to bf16; keys are paged like the latent cache (64-token blocks, one
+# random block permutation over all sequences); the cache is filled completely.
+
+@dataclasses.dataclass(frozen=True)
+class IndexerWorkload:
+    name: str
+    batch: int
+    q_len: int
+    topk: int
+    seq_len: Optional[int] = None
+    seq_len_range: Optional[tuple] = None
+    d_idx: int = 128
+    block_size: int = 64
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.q_len
+
+    @property
+    def max_seq_len(self) -> int:
+        return self.seq_len if self.seq_len is not None else self.seq_len_range[1]
+
+
+INDEXER_WORKLOADS = [
+    # the pages' decode step after the context cap: top-512 over 8192-token contexts at batch 64
+    IndexerWorkload("idx_b64_topk512_n8192", batch=64, q_len=1, topk=512, seq_len=8192),
+    # the latent-cache workloads' sizes: top-2048 over 65536-token contexts at batch 16
+    IndexerWorkload("idx_b16_topk2048_n65536", batch=16, q_len=1, topk=2048, seq_len=65536),
+]
+INDEXER_WORKLOADS_BY_NAME = {w.name: w for w in INDEXER_WORKLOADS}
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    workload: IndexerWorkload
+    q_idx: np.ndarray        # uint16 [B, q_len, d_idx] bf16 bits
+    k_cache: np.ndarray      # uint16 [num_blocks, block_size, d_idx] bf16 bits
+    block_table: np.ndarray  # int32 [B, max_blocks]
+    seq_lens: np.ndarray     # int32 [B]
+
+    def candidate_count(self) -> int:
+        return int(np.minimum(self.seq_lens.astype(np.int64),
+                              self.workload.block_size * self.block_table.shape[1]).sum())
+
+
+def make_indexer_inputs(w: IndexerWorkload, seed: int = 0) -> IndexerInputs:
+    streams = [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(4)]
+    r_len, r_blk, r_q, r_k = streams
+    B, bs = w.batch, w.block_size
+    if w.seq_len is not None:
+        seq_lens = np.full(B, w.seq_len, dtype=np.int32)
+    else:
+        lo, hi = w.seq_len_range
+        seq_lens = r_len.integers(lo, hi + 1, size=B).astype(np.int32)
+    max_blocks = (w.max_seq_len + bs - 1) // bs
+    nblk = (seq_lens.astype(np.int64) + bs - 1) // bs
+    total = int(nblk.sum())
+    block_table = np.zeros((B, max_blocks), dtype=np.int32)
+    phys = r_blk.permutation(total)
+    off = 0
+    for b in range(B):
+        block_table[b, : nblk[b]] = phys[off: off + nblk[b]]
+        off += int(nblk[b])
+    q_idx = bf16_bits_rne(r_q.standard_normal((B, w.q_len, w.d_idx), dtype=np.float32))
+    k_cache = np.empty((total, bs, w.d_idx), dtype=np.uint16)
+    flat = k_cache.reshape(-1, w.d_idx)
+    chunk = 1 << 18
+    for start in range(0, flat.shape[0], chunk):
+        n = min(chunk, flat.shape[0] - start)
+        flat[start: start + n] = bf16_bits_rne(r_k.standard_normal((n, w.d_idx), dtype=np.float32))
+    return IndexerInputs(workload=w, q_idx=q_idx, k_cache=k_cache, block_table=block_table, seq_lens=seq_lens)
+
+
+def small_indexer_inputs(batch=2, q_len=1, topk=64, seq_len=300, seed=0, seq_len_range=None,
+                         d_idx=128) -> IndexerInputs:
+    w = IndexerWorkload(f"small_idx_b{batch}_q{q_len}_topk{topk}_n{seq_len}", batch=batch, q_len=q_len, topk=topk,
+                        seq_len=None if seq_len_range else seq_len, seq_len_range=seq_len_range, d_idx=d_idx)
+    return make_indexer_inputs(w, seed=seed)

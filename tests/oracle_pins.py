@@ -11,7 +11,9 @@ the oracle disagrees with:
   paged cache, masking by -1 / out-of-range entries;
 * closed forms: a single selected token, a zero query, identical rows,
   repeated indices, and the combine's own special cases;
-* library conversions (torch) of every bf16, e4m3fn and UE8M0 bit pattern.
+* library conversions (torch) of every bf16, e4m3fn and UE8M0 bit pattern;
+* for the top-k indexer: numpy matmul scores over keys decoded here, a numpy
+  lexsort selection, a closed form with ties, masking and block placement.
 
 kv_format 2 (the pages' paged layout: per block, the 576-byte token rows,
 then the 8-byte scale records) is decoded here with numpy slicing of the
@@ -405,9 +407,108 @@ def pin_combine_closed_forms(orc):
     assert np.all(co == 0.0) and np.all(cl == -np.inf), "all parts empty: (0, -inf)"
 
 
+# ----------------------------------------------------------------- top-k indexer
+
+
+def _np_indexer_scores(inp):
+    """Scores [B, q_len, cap] by a numpy matmul over keys decoded here; -inf where not a candidate."""
+    w = inp.workload
+    bs, mb = w.block_size, inp.block_table.shape[1]
+    cap = bs * mb
+    K = np_bf16(inp.k_cache)                                  # [blocks, bs, d]
+    out = np.full((w.batch, w.q_len, cap), -np.inf)
+    for b in range(w.batch):
+        n = min(int(inp.seq_lens[b]), cap)
+        pos = np.arange(n)
+        blk = inp.block_table[b, pos // bs]
+        ok = (blk >= 0) & (blk < inp.k_cache.shape[0])
+        Kb = K[blk[ok], pos[ok] % bs]                         # [n_ok, d]
+        out[b][:, pos[ok]] = np_bf16(inp.q_idx[b]) @ Kb.T
+    return out
+
+
+def _np_topk(scores, k):
+    """Positions of the k highest scores (ties: lower position first), -1 past the candidates."""
+    B, Q, cap = scores.shape
+    idx = np.full((B, Q, k), -1, dtype=np.int64)
+    for b in range(B):
+        for q in range(Q):
+            s = scores[b, q]
+            cand = np.nonzero(np.isfinite(s))[0]
+            order = cand[np.lexsort((cand, -s[cand]))]      # primary: score descending, then position
+            take = order[:k]
+            idx[b, q, : len(take)] = take
+    return idx
+
+
+def pin_indexer_scores_dense(orc):
+    inp = I.small_indexer_inputs(batch=3, q_len=2, topk=40, seq_len_range=(50, 300), seed=20)
+    sc, ab = orc.indexer_scores(inp.q_idx, inp.k_cache, inp.block_table, inp.seq_lens)
+    ref = _np_indexer_scores(inp)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(sc), fin), "candidate positions differ"
+    assert_close(sc[fin], ref[fin], 1e-13, "indexer scores")
+    assert np.all(ab[fin] >= np.abs(sc[fin]) - 1e-9) and np.all(ab[~fin] == 0)
+
+
+def pin_indexer_topk_matches_sort(orc):
+    for seed, k in ((21, 64), (22, 300)):                    # 300 > some sequences: -1 padding
+        inp = I.small_indexer_inputs(batch=3, q_len=2, topk=k, seq_len_range=(100, 400), seed=seed)
+        idx, sc = orc.indexer_topk(inp.q_idx, inp.k_cache, inp.block_table, inp.seq_lens, k)
+        ref_scores = _np_indexer_scores(inp)
+        ref = _np_topk(ref_scores, k)
+        assert np.array_equal(idx, ref), f"selection differs from a sort of numpy scores (k={k})"
+        fin = ref >= 0
+        got = np.take_along_axis(ref_scores, np.maximum(ref, 0), axis=2)
+        assert_close(sc[fin], got[fin], 1e-13, "selected scores")
+        assert np.all(np.isneginf(sc[~fin]))
+
+
+def pin_indexer_ties_and_closed_form(orc):
+    # q = e_0 and key[p][0] = v(p): the scores are the v(p) exactly; repeated values tie
+    inp = I.small_indexer_inputs(batch=1, q_len=1, topk=10, seq_len=128, seed=23)
+    q = np.zeros_like(inp.q_idx)
+    q[0, 0, 0] = 0x3F80                                       # 1.0
+    k = np.zeros_like(inp.k_cache)
+    vals = np.array([(p * 37) % 11 for p in range(128)], dtype=np.float32)   # 0..10, many ties
+    bs = 64
+    for p in range(128):
+        k[inp.block_table[0, p // bs], p % bs, 0] = I.bf16_bits_rne(vals[p:p + 1])[0]
+    idx, sc = orc.indexer_topk(q, k, inp.block_table, inp.seq_lens, 25)
+    expect = sorted(range(128), key=lambda p: (-vals[p], p))[:25]
+    assert idx[0, 0].tolist() == expect, "ties must go to the lower position"
+    assert np.array_equal(sc[0, 0], vals[expect].astype(np.float64))
+
+
+def pin_indexer_masking_and_paging(orc):
+    inp = I.small_indexer_inputs(batch=2, q_len=1, topk=80, seq_len=256, seed=24)
+    bt = inp.block_table.copy()
+    sl = inp.seq_lens.copy()
+    sl[0] = 150                                               # positions 150.. of sequence 0 excluded
+    bt[1, 1] = -3                                             # positions 64..127 of sequence 1 excluded
+    bt[1, 3] = inp.k_cache.shape[0] + 2                       # positions 192..255 too
+    idx, _ = orc.indexer_topk(inp.q_idx, inp.k_cache, bt, sl, 200)
+    assert (idx[0, 0] >= 0).sum() == 150 and idx[0, 0, :150].max() < 150 and np.all(idx[0, 0, 150:] == -1)
+    v1 = idx[1, 0][idx[1, 0] >= 0]
+    assert len(v1) == 128 and not np.any((v1 >= 64) & (v1 < 128)) and not np.any(v1 >= 192)
+    # moving the blocks and their table entries together changes nothing
+    nb = inp.k_cache.shape[0]
+    perm = np.random.default_rng(25).permutation(nb)
+    k2 = np.empty_like(inp.k_cache)
+    k2[perm] = inp.k_cache
+    bt2 = perm[inp.block_table].astype(np.int32)
+    a = orc.indexer_topk(inp.q_idx, inp.k_cache, inp.block_table, inp.seq_lens, 80)
+    c = orc.indexer_topk(inp.q_idx, k2, bt2, inp.seq_lens, 80)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1]), "block placement changed the selection"
+    e = orc.indexer_topk(inp.q_idx, inp.k_cache, inp.block_table, np.zeros_like(inp.seq_lens), 5)
+    assert np.all(e[0] == -1), "no candidates: all -1"
+
+
 ALL_PINS = [
     pin_bf16_table, pin_e4m3_table, pin_ue8m0_table, pin_dense_bf16, pin_dense_fp8, pin_dense_v4,
     pin_dense_ragged_padded, pin_permutation, pin_split_combine, pin_paging, pin_paging_v4, pin_masking,
     pin_seq_lens_mask, pin_empty_row, pin_single_token, pin_single_token_v4, pin_zero_query,
     pin_identical_rows, pin_identical_rows_v4, pin_duplicates, pin_combine_closed_forms,
+    pin_indexer_scores_dense, pin_indexer_topk_matches_sort, pin_indexer_ties_and_closed_form,
+    pin_indexer_masking_and_paging,
 ]

@@ -110,3 +110,13 @@ def test_v4_selected_fill():
     p = inp.indices[0, 0].astype(np.int64)
     blk = inp.block_table[0, p // bs]
     assert np.all(rec[blk, p % bs, :7] > 0), "a selected token's scale record was left unfilled"
+
+
+def test_indexer_inputs_recipe():
+    w = I.INDEXER_WORKLOADS_BY_NAME["idx_b64_topk512_n8192"]
+    a = I.make_indexer_inputs(w)
+    assert a.q_idx.shape == (64, 1, 128) and a.k_cache.shape == (64 * 128, 64, 128)
+    assert sorted(a.block_table.reshape(-1).tolist()) == list(range(64 * 128)), "paged: one permutation"
+    assert a.candidate_count() == 64 * 8192
+    b = I.make_indexer_inputs(w)
+    assert np.array_equal(a.k_cache[:3], b.k_cache[:3]) and np.array_equal(a.q_idx, b.q_idx)

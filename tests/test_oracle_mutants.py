@@ -71,6 +71,21 @@ MUTATIONS = [
     ("token rows strided by the 584-byte slot",
      "const uint8_t *row = block + (int64_t)slot * V4_DATA_BYTES;",
      "const uint8_t *row = block + (int64_t)slot * (V4_DATA_BYTES + V4_SCALE_BYTES);"),
+    ("indexer ties go to the higher position",
+     "return sa > sb || (sa == sb && pa < pb);",
+     "return sa > sb || (sa == sb && pa > pb);"),
+    ("indexer keeps the lowest scores",
+     "return sa > sb || (sa == sb && pa < pb);",
+     "return sa < sb || (sa == sb && pa < pb);"),
+    ("indexer ignores seq_lens",
+     "    if ((int64_t)seq_lens[b] < cap) cap = seq_lens[b];\n",
+     ""),
+    ("indexer key rows strided by half a row",
+     "const int64_t row_bytes = 2 * (int64_t)d_idx;",
+     "const int64_t row_bytes = (int64_t)d_idx;"),
+    ("indexer drops the last key dimension",
+     "    for (int d = 0; d < d_idx; ++d) {\n        double t = oracle_bf16_to_f64(q[d])",
+     "    for (int d = 0; d < d_idx - 1; ++d) {\n        double t = oracle_bf16_to_f64(q[d])"),
     ("seq_lens ignored",
      "if (J->seq_lens && (int64_t)J->seq_lens[b] < cap) cap = J->seq_lens[b];",
      ""),
