@@ -409,9 +409,10 @@ int oracle_lse_combine(int32_t num_splits, int64_t n, int32_t d_v, const double 
  *     score(r, p) = sum_{d < d_idx} q_idx[r, d] * k_idx[block_table[b][p / bs], p % bs, d]
  * over the candidate positions of sequence b: 0 <= p < min(seq_lens[b],
  * bs * max_blocks_per_seq) whose block-table entry lies in [0, num_kv_blocks).
- * The selection is the min(topk, #candidates) positions of highest score,
- * ordered by score, highest first, equal scores by position, lowest first;
- * the rest of the row's list is -1.
+ * The selection is the min(topk, #candidates) positions of highest score
+ * (among equal scores the lower positions first), listed in ascending
+ * position order (the pages give no order; the attention that consumes the
+ * list does not depend on it); the rest of the row's list is -1.
  */
 
 static double indexer_score(const uint16_t *q, const uint8_t *kcache, int64_t row_bytes, int64_t phys, int32_t d_idx,
@@ -481,10 +482,11 @@ static int ranks_before(double sa, int64_t pa, double sb, int64_t pb)
 }
 
 /*
- * The selection: out_idx [batch, q_len, topk] int32 positions and
- * out_score [batch, q_len, topk] fp64 (or NULL), -1 / -inf past the
- * candidates.  A plain selection: for each slot j the best candidate not yet
- * taken (O(topk * cap) per row; test sizes only).
+ * The selection: out_idx [batch, q_len, topk] int32 positions in ascending
+ * order and out_score [batch, q_len, topk] fp64 (or NULL), -1 / -inf past
+ * the candidates.  A plain selection: repeatedly the best candidate not yet
+ * taken (O(topk * cap) per row; test sizes only), then the taken positions
+ * in ascending order.
  */
 int oracle_indexer_topk(int32_t batch, int32_t q_len, int32_t d_idx, int32_t block_size, int32_t max_blocks_per_seq,
                         int64_t num_kv_blocks, const uint16_t *q_idx, const uint8_t *k_cache,
@@ -513,9 +515,19 @@ int oracle_indexer_topk(int32_t batch, int32_t q_len, int32_t d_idx, int32_t blo
                 if (taken[p] || s[p] == -INFINITY) continue;
                 if (best < 0 || ranks_before(s[p], p, s[best], best)) best = p;
             }
-            out_idx[r * topk + j] = best < 0 ? -1 : (int32_t)best;
-            if (out_score) out_score[r * topk + j] = best < 0 ? -INFINITY : s[best];
-            if (best >= 0) taken[best] = 1;
+            if (best < 0) break;
+            taken[best] = 1;
+        }
+        int32_t j = 0;
+        for (int64_t p = 0; p < cap; ++p) {
+            if (!taken[p]) continue;
+            out_idx[r * topk + j] = (int32_t)p;
+            if (out_score) out_score[r * topk + j] = s[p];
+            ++j;
+        }
+        for (; j < topk; ++j) {
+            out_idx[r * topk + j] = -1;
+            if (out_score) out_score[r * topk + j] = -INFINITY;
         }
     }
     free(sc);

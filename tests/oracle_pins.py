@@ -428,7 +428,7 @@ def _np_indexer_scores(inp):
 
 
 def _np_topk(scores, k):
-    """Positions of the k highest scores (ties: lower position first), -1 past the candidates."""
+    """Positions of the k highest scores (ties: lower position first) in ascending order, -1 past the candidates."""
     B, Q, cap = scores.shape
     idx = np.full((B, Q, k), -1, dtype=np.int64)
     for b in range(B):
@@ -436,7 +436,7 @@ def _np_topk(scores, k):
             s = scores[b, q]
             cand = np.nonzero(np.isfinite(s))[0]
             order = cand[np.lexsort((cand, -s[cand]))]      # primary: score descending, then position
-            take = order[:k]
+            take = np.sort(order[:k])
             idx[b, q, : len(take)] = take
     return idx
 
@@ -475,7 +475,7 @@ def pin_indexer_ties_and_closed_form(orc):
     for p in range(128):
         k[inp.block_table[0, p // bs], p % bs, 0] = I.bf16_bits_rne(vals[p:p + 1])[0]
     idx, sc = orc.indexer_topk(q, k, inp.block_table, inp.seq_lens, 25)
-    expect = sorted(range(128), key=lambda p: (-vals[p], p))[:25]
+    expect = sorted(sorted(range(128), key=lambda p: (-vals[p], p))[:25])
     assert idx[0, 0].tolist() == expect, "ties must go to the lower position"
     assert np.array_equal(sc[0, 0], vals[expect].astype(np.float64))
 

@@ -77,6 +77,9 @@ MUTATIONS = [
     ("indexer keeps the lowest scores",
      "return sa > sb || (sa == sb && pa < pb);",
      "return sa < sb || (sa == sb && pa < pb);"),
+    ("indexer list not in position order",
+     "        for (int64_t p = 0; p < cap; ++p) {\n            if (!taken[p]) continue;",
+     "        for (int64_t p = cap - 1; p >= 0; --p) {\n            if (!taken[p]) continue;"),
     ("indexer ignores seq_lens",
      "    if ((int64_t)seq_lens[b] < cap) cap = seq_lens[b];\n",
      ""),
