@@ -20,6 +20,13 @@ the partial-attention kernel alone, timed the same way from a graph of K
 ``smla_decode_partial`` calls (the combine kernel is timed from a graph of
 K ``smla_combine`` calls).  ``cpu_baseline`` times the fp64 oracle on the
 host for a bounded sample.
+
+``--workload idx_...`` measures the top-k indexer instead (one step = one
+``smla_indexer_topk`` call: the score kernel streams every candidate's
+indexer key, the select kernel picks the top-k per row): ``value`` = key
+bytes / call time, ``roofline`` for the score kernel alone (timed from a
+graph of ``smla_indexer_scores`` calls), cold cache by rotating copies of the
+key cache the same way.
 """
 from __future__ import annotations
 
@@ -40,15 +47,21 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b1_topk2048_n32768_paged_bf16"
 ROTATION_BYTES = 1 << 30
 MAX_COPY_BYTES = 48 << 30
+INDEXER_METRIC = "top-k indexer µs/call + indexer-key HBM GB/s (% peak)"
 KERNEL_SOURCES = ["sparse_mla_decode_smla_amd/csrc/smla_decode.hip",
                   "sparse_mla_decode_smla_amd/csrc/smla_combine.hip",
                   "sparse_mla_decode_smla_amd/csrc/smla_internal.h",
                   "sparse_mla_decode_smla_amd/csrc/smla_plan.cpp"]
+INDEXER_SOURCES = ["sparse_mla_decode_smla_amd/csrc/smla_indexer.hip"]
 
 
-def kernel_source_hash() -> str:
+def is_indexer(workload: str) -> bool:
+    return workload.startswith("idx_")
+
+
+def kernel_source_hash(workload: str = DEFAULT_WORKLOAD) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (INDEXER_SOURCES if is_indexer(workload) else KERNEL_SOURCES):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -65,12 +78,13 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
 
 PARTIAL_KERNEL = "partial_kernel"
+SCORE_KERNEL = "score_kernel"
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -111,15 +125,16 @@ def _counter_means(csv_dir: str, counter: str, name_part: str) -> tuple[float, i
 def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
                     copy_write_dir: str, command: str) -> int:
     """Turn FETCH_SIZE / WRITE_SIZE counter runs (KiB per dispatch) into HBM bytes per partial launch."""
-    fetch_kib, nf = _counter_means(fetch_dir, "FETCH_SIZE", PARTIAL_KERNEL)
-    write_kib, nw = _counter_means(write_dir, "WRITE_SIZE", PARTIAL_KERNEL)
+    kernel = SCORE_KERNEL if is_indexer(workload) else PARTIAL_KERNEL
+    fetch_kib, nf = _counter_means(fetch_dir, "FETCH_SIZE", kernel)
+    write_kib, nw = _counter_means(write_dir, "WRITE_SIZE", kernel)
     cf_kib, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "elementwise")
     cw_kib, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "elementwise")
     f_scale = COPY_PROBE_BYTES / (cf_kib * 1024.0)
     w_scale = COPY_PROBE_BYTES / (cw_kib * 1024.0)
     fetch_b = fetch_kib * 1024.0 * f_scale
     write_b = write_kib * 1024.0 * w_scale
-    rec = {"workload": workload, "kernel": PARTIAL_KERNEL, "kernel_source_hash": kernel_source_hash(),
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(workload),
            "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
            "bytes_per_launch": round(fetch_b + write_b), "dispatches": {"fetch": nf, "write": nw},
            "raw_kib_per_dispatch": {"FETCH_SIZE": fetch_kib, "WRITE_SIZE": write_kib},
@@ -160,6 +175,120 @@ def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
                       f"{el:.1f} s fp64 on the host"}
 
 
+def _graph_timer(torch, stream, K):
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(K):
+                    fn(i)
+        return g
+
+    def time_graph(g) -> float:
+        g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            g.replay()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) * 1e3 / K
+    return capture, time_graph
+
+
+def bench_indexer(args) -> int:
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_mla_decode_smla_amd import binding as B
+    from sparse_mla_decode_smla_amd import inputs as I
+
+    w = I.INDEXER_WORKLOADS_BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}")
+    inp = I.make_indexer_inputs(w)
+    key_bytes = inp.candidate_count() * 2 * w.d_idx          # each candidate's key, read once per sequence
+    q, k, bt, sl = B.indexer_to_device(inp, device=dev)
+    mb = bt.shape[1]
+    R = max(2, min(math.ceil(ROTATION_BYTES / key_bytes), MAX_COPY_BYTES // max(k.numel() * 2, 1), 64))
+    log(f"[bench] key bytes {key_bytes}, key-cache copies for rotation: {R}")
+    copies = [k] + [k.clone() for _ in range(R - 1)]
+    idx = torch.empty((w.batch, w.q_len, w.topk), dtype=torch.int32, device=dev)
+    sc = torch.empty((w.batch, w.q_len, w.topk), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.indexer_workspace_size(w.batch, w.q_len, mb), dtype=torch.uint8, device=dev)
+    scores = ws.view(torch.float32)
+
+    def step(i):
+        B.indexer_topk(q, copies[i % R], bt, sl, w.topk, out_indices=idx, out_scores=sc, workspace=ws)
+
+    def step_scores(i):
+        B.indexer_scores(q, copies[i % R], bt, sl, scores)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_idx = idx.clone()
+    K = args.steps
+    stream = torch.cuda.Stream(device=dev)
+    capture, time_graph = _graph_timer(torch, stream, K)
+    g = capture(step)
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(idx, ref_idx):
+        log("[bench] graph replay result differs from the eager result")
+        return 1
+    call_us = time_graph(g)
+    del g
+    score_us = time_graph(capture(step_scores))
+    gbs = key_bytes / (call_us * 1e-6) / 1e9
+    kernel_gbs = key_bytes / (score_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.indexer_topk(inp.q_idx[:1], inp.k_cache, inp.block_table[:1], inp.seq_lens[:1], w.topk)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        sample = int(min(inp.seq_lens[0], 64 * mb)) * 2 * w.d_idx * w.q_len * reps
+        cpu = {"value": round(sample / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} x sequence 0 ({w.q_len} query row(s)) of the workload, {el:.1f} s fp64 on the "
+                         "host (scores and selection)"}
+    line = {
+        "metric": INDEXER_METRIC,
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(call_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "topk": w.topk, "d_idx": w.d_idx,
+                   "seq_len": w.seq_len if w.seq_len else list(w.seq_len_range), "key_bytes": key_bytes,
+                   "cache": f"cold: {R} rotating key-cache copies"},
+        "us_per_call": round(call_us, 3),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kernels_us": {"score": round(score_us, 3), "select (call minus score)": round(call_us - score_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +322,8 @@ def main() -> int:
     from sparse_mla_decode_smla_amd import binding as B
     from sparse_mla_decode_smla_amd import inputs as I
 
+    if is_indexer(args.workload):
+        return bench_indexer(args)
     w = I.WORKLOADS_BY_NAME[args.workload]
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")

@@ -181,6 +181,53 @@ smla_status_t smla_decode_partial(const smla_plan_t *plan, const void *q, const 
 smla_status_t smla_combine(const float *part_out, const float *part_lse, int32_t num_splits, int32_t rows,
                            int32_t num_heads, int32_t d_v, void *out, float *lse, void *stream);
 
+/*
+ * Top-k indexer: the step that produces the index lists ("The Pivot Point:
+ * When a 6.3x Kernel Speedup Reveals the Next Bottleneck", Input Knowledge
+ * Required: an indexer selects the top ~512 cache positions of each decode
+ * step; "The Moment of Truth: Benchmarking a Custom MMA Kernel for
+ * DeepSeek-V4-Flash on Blackwell", The Broader Context: it scores every
+ * position of the context; "The MMA Sparse-MLA Decode Kernel: A Deep Dive
+ * into AI Inference Optimization on Blackwell GPUs", Context: a batched
+ * product of the indexer query with the indexer keys).
+ *   q_idx        bf16  [batch, q_len, d_idx]
+ *   k_cache      bf16  [num_kv_blocks, block_size, d_idx]: indexer keys, paged
+ *                with the same block table as the latent cache
+ *   block_table  int32 [batch, max_blocks_per_seq];  seq_lens int32 [batch] (required)
+ *   out_indices  int32 [batch, q_len, topk]: logical positions, ready to be
+ *                the `indices` of smla_decode_run
+ *   out_scores   fp32  [batch, q_len, topk] or NULL
+ *   workspace    >= smla_indexer_workspace_size(...) bytes, 16-byte aligned:
+ *                fp32 scores [batch * q_len, block_size * max_blocks_per_seq]
+ * For row (b, s) the candidates are the positions p < min(seq_lens[b],
+ * block_size * max_blocks_per_seq) whose block-table entry lies in
+ * [0, num_kv_blocks); score(p) = q_idx[b, s, :] . key(p), bf16 products
+ * accumulated in fp32.  The row's list is the min(topk, #candidates)
+ * positions of highest score (among equal scores the lower positions), in
+ * ascending position order, then -1 (out_scores -inf).  Scores must be
+ * finite (finite inputs).
+ * Supported: d_idx = 128, block_size = 64, 1 <= q_len <= 4,
+ * 0 <= topk <= 2048 (else SMLA_ERR_UNSUPPORTED).  Pointer alignment: q_idx
+ * and k_cache 16 bytes, the int32/fp32 arrays 4 bytes (else
+ * SMLA_ERR_INVALID_ARG).  Two kernels on `stream` (scores, then the
+ * selection); asynchronous; allocates nothing; the launch geometry depends
+ * only on the sizes.
+ */
+smla_status_t smla_indexer_workspace_size(int32_t batch, int32_t q_len, int32_t block_size,
+                                          int32_t max_blocks_per_seq, uint64_t *bytes_out);
+/* The first half of smla_indexer_topk alone: the scores of every candidate
+ * into scores fp32 [batch * q_len, block_size * max_blocks_per_seq] (caller's
+ * buffer, 4-byte aligned): position p < min(seq_lens[b], block_size *
+ * max_blocks_per_seq) gets its score, or -inf if its block-table entry is out
+ * of range; later positions are not written.  Same shape and pointer rules. */
+smla_status_t smla_indexer_scores(const void *q_idx, int32_t d_idx, const void *k_cache, int64_t num_kv_blocks,
+                                  const int32_t *block_table, const int32_t *seq_lens, int32_t batch, int32_t q_len,
+                                  int32_t block_size, int32_t max_blocks_per_seq, float *scores, void *stream);
+smla_status_t smla_indexer_topk(const void *q_idx, int32_t d_idx, const void *k_cache, int64_t num_kv_blocks,
+                                const int32_t *block_table, const int32_t *seq_lens, int32_t batch, int32_t q_len,
+                                int32_t block_size, int32_t max_blocks_per_seq, int32_t topk, int32_t *out_indices,
+                                float *out_scores, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code (host). */
 const char *smla_status_string(smla_status_t status);
 

@@ -74,6 +74,15 @@ def load(path: Optional[str] = None):
     lib.smla_decode_partial.restype = ctypes.c_int
     lib.smla_combine.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.smla_combine.restype = ctypes.c_int
+    lib.smla_indexer_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.POINTER(ctypes.c_uint64)]
+    lib.smla_indexer_workspace_size.restype = ctypes.c_int
+    lib.smla_indexer_topk.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, P, P, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+    lib.smla_indexer_topk.restype = ctypes.c_int
+    lib.smla_indexer_scores.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, P, P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.smla_indexer_scores.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int]
     lib.smla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -199,3 +208,57 @@ def sparse_mla_decode(q, kv_cache, block_table, indices, seq_lens, softmax_scale
     ws = alloc_workspace(plan, q.device)
     decode_run(plan, q, kv_cache, block_table, indices, seq_lens, softmax_scale, out, lse, ws, stream)
     return out, lse
+
+
+# ----------------------------------------------------------------- top-k indexer
+
+
+def indexer_workspace_size(batch: int, q_len: int, max_blocks_per_seq: int, block_size: int = 64) -> int:
+    n = ctypes.c_uint64(0)
+    _check(load().smla_indexer_workspace_size(batch, q_len, block_size, max_blocks_per_seq, ctypes.byref(n)),
+           "smla_indexer_workspace_size")
+    return int(n.value)
+
+
+def indexer_topk(q_idx, k_cache, block_table, seq_lens, topk: int, out_indices=None, out_scores=None,
+                 workspace=None, stream=None, with_scores: bool = True):
+    """Enqueue smla_indexer_topk; returns (indices int32 [B, q_len, topk], scores fp32 or None).
+
+    q_idx bf16 [B, q_len, d_idx]; k_cache bf16 [num_blocks, 64, d_idx]; block_table int32 [B, max_blocks];
+    seq_lens int32 [B].  Output and workspace tensors are allocated with torch when not given."""
+    import torch
+    B, q_len, d_idx = q_idx.shape
+    mb = block_table.shape[1]
+    if out_indices is None:
+        out_indices = torch.empty((B, q_len, topk), dtype=torch.int32, device=q_idx.device)
+    if out_scores is None and with_scores:
+        out_scores = torch.empty((B, q_len, topk), dtype=torch.float32, device=q_idx.device)
+    if workspace is None:
+        workspace = torch.empty(max(indexer_workspace_size(B, q_len, mb, k_cache.shape[1]), 16), dtype=torch.uint8,
+                                device=q_idx.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().smla_indexer_topk(_ptr(q_idx), d_idx, _ptr(k_cache), k_cache.shape[0], _ptr(block_table),
+                                    _ptr(seq_lens), B, q_len, k_cache.shape[1], mb, topk, _ptr(out_indices),
+                                    _ptr(out_scores), _ptr(workspace), ws_bytes, _stream(stream)),
+           "smla_indexer_topk")
+    return out_indices, out_scores
+
+
+def indexer_scores(q_idx, k_cache, block_table, seq_lens, scores, stream=None) -> None:
+    """Enqueue smla_indexer_scores into `scores` fp32 [B * q_len, 64 * max_blocks]."""
+    B, q_len, d_idx = q_idx.shape
+    _check(load().smla_indexer_scores(_ptr(q_idx), d_idx, _ptr(k_cache), k_cache.shape[0], _ptr(block_table),
+                                      _ptr(seq_lens), B, q_len, k_cache.shape[1], block_table.shape[1],
+                                      _ptr(scores), _stream(stream)),
+           "smla_indexer_scores")
+
+
+def indexer_to_device(inp, device="cuda"):
+    """Device tensors (q_idx, k_cache, block_table, seq_lens) of ``inputs.IndexerInputs``."""
+    import numpy as np
+    import torch
+    q = torch.from_numpy(inp.q_idx.view(np.int16)).view(torch.bfloat16).to(device)
+    k = torch.from_numpy(inp.k_cache.view(np.int16)).view(torch.bfloat16).to(device)
+    bt = torch.from_numpy(inp.block_table).to(device)
+    sl = torch.from_numpy(inp.seq_lens).to(device)
+    return q, k, bt, sl

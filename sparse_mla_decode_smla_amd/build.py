@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libsmla.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("smla_plan.cpp", "smla_decode.hip", "smla_combine.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f)
+           for f in ("smla_plan.cpp", "smla_decode.hip", "smla_combine.hip", "smla_indexer.hip")]
 INCLUDE = [os.path.join(ROOT, "include"), os.path.join(HERE, "csrc")]
 ARCH = "gfx950"
 

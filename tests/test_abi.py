@@ -23,7 +23,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"smla_decode_plan", "smla_decode_run", "smla_decode_partial", "smla_combine",
-                          "smla_status_string"}
+                          "smla_status_string", "smla_indexer_workspace_size", "smla_indexer_topk",
+                          "smla_indexer_scores"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in smla.h but not exported"
@@ -167,3 +168,29 @@ def test_combine_argument_checks_need_no_gpu():
     assert lib.smla_combine(None, 1 << 21, 2, 1, 64, 512, 1 << 22, 1 << 23, None) == 1
     assert lib.smla_combine((1 << 20) + 8, 1 << 21, 2, 1, 64, 512, 1 << 22, 1 << 23, None) == 1  # misaligned
     assert lib.smla_combine(1 << 20, 1 << 21, 2, 1, 64, 512, (1 << 22) + 8, 1 << 23, None) == 1
+
+
+def test_indexer_argument_checks_need_no_gpu():
+    lib = B.load()
+    assert B.indexer_workspace_size(3, 2, 10) == 3 * 2 * 640 * 4
+    n = ctypes.c_uint64(0)
+    assert lib.smla_indexer_workspace_size(-1, 1, 64, 10, ctypes.byref(n)) == 1
+    assert lib.smla_indexer_workspace_size(1, 1, 64, 10, None) == 1
+
+    def call(**kw):
+        a = dict(q=1 << 20, d=128, k=1 << 21, nb=16, bt=1 << 22, sl=1 << 23, B=2, Q=1, bs=64, mb=8, topk=64,
+                 oi=1 << 24, os=1 << 25, ws=1 << 26, wsb=2 * 512 * 4)
+        a.update(kw)
+        return lib.smla_indexer_topk(a["q"], a["d"], a["k"], a["nb"], a["bt"], a["sl"], a["B"], a["Q"], a["bs"],
+                                     a["mb"], a["topk"], a["oi"], a["os"], a["ws"], a["wsb"], None)
+    assert call(d=64) == 2 and call(bs=32) == 2 and call(topk=4096) == 2 and call(Q=5) == 2
+    assert call(topk=-1) == 1 and call(mb=0) == 1 and call(nb=-1) == 1
+    assert call(q=None) == 1 and call(sl=None) == 1 and call(oi=None) == 1
+    assert call(wsb=2 * 512 * 4 - 1) == 3 and call(ws=None) == 3
+    assert call(q=(1 << 20) + 8) == 1 and call(k=(1 << 21) + 4) == 1 and call(oi=(1 << 24) + 2) == 1
+    assert call(B=0, q=None, oi=None) == 0 and call(topk=0, oi=None) == 0   # nothing to do
+    assert call(topk=0, q=None) == 1                                          # still checked
+    assert lib.smla_indexer_scores(1 << 20, 128, 1 << 21, 16, 1 << 22, 1 << 23, 2, 1, 64, 8, None, None) == 1
+    assert lib.smla_indexer_scores(1 << 20, 128, 1 << 21, 16, 1 << 22, 1 << 23, 2, 1, 64, 8, (1 << 24) + 2,
+                                   None) == 1
+    assert lib.smla_indexer_scores(1 << 20, 96, 1 << 21, 16, 1 << 22, 1 << 23, 2, 1, 64, 8, 1 << 24, None) == 2
