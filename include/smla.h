@@ -108,7 +108,8 @@ typedef struct {
     int32_t tile_tokens;         /* tokens per gathered tile */
     int32_t heads_per_group;     /* heads served by one workgroup */
     int32_t num_workgroups;      /* workgroups of the partial-attention kernel */
-    uint64_t workspace_bytes;    /* bytes of device workspace smla_decode_run needs (0 if S = 1) */
+    uint64_t workspace_bytes;    /* bytes of device workspace smla_decode_run needs (0 if S = 1):
+                                    S * rows * H * (2 * d_v + 4) */
 } smla_plan_t;
 
 /*
@@ -154,10 +155,12 @@ smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void
  * the same way; "The Moment of Truth: Analyzing a Custom MMA Kernel's
  * Performance on Blackwell GPUs", "The Split-K Solution: Reasoning About the
  * Fix"), laid out as
- *   part_out = (float *)workspace                   fp32 [S, R, H, d_v]
- *   part_lse = part_out + S * R * H * d_v           fp32 [S, R, H]
+ *   part_out = (uint16_t *)workspace                bf16 [S, R, H, d_v]
+ *   part_lse = (float *)(part_out + S * R * H * d_v) fp32 [S, R, H]
  * with S = plan->num_splits; out and lse are then not written.  An empty
- * part has part_lse = -inf and part_out = 0.
+ * part has part_lse = -inf and part_out = 0.  The partial outputs are
+ * rounded to bf16 (fp32 accumulation, one rounding more than the final
+ * output; the combine adds them in fp32): half the bytes of fp32 partials.
  */
 smla_status_t smla_decode_partial(const smla_plan_t *plan, const void *q, const void *kv_cache,
                                   int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,
@@ -168,17 +171,17 @@ smla_status_t smla_decode_partial(const smla_plan_t *plan, const void *q, const 
  * Log-sum-exp merge of partial attention results over disjoint parts of a
  * list ("The Moment of Truth: Analyzing a Custom MMA Kernel's Performance
  * on Blackwell GPUs", "The Split-K Solution: Reasoning About the Fix").
- *   part_out  fp32 [num_splits, rows, num_heads, d_v]: per-part normalised outputs
+ *   part_out  bf16 [num_splits, rows, num_heads, d_v]: per-part normalised outputs
  *   part_lse  fp32 [num_splits, rows, num_heads]: per-part lse, -inf for an empty part
  *   out       bf16 [rows, num_heads, d_v];  lse fp32 [rows, num_heads]
- * out = sum_i exp(lse_i - lse) * part_out_i with lse = ln sum_i exp(lse_i);
+ * out = sum_i exp(lse_i - lse) * part_out_i with lse = ln sum_i exp(lse_i), in fp32;
  * parts with lse_i = -inf carry no weight and their part_out values are
  * ignored (even NaN); if every part is empty, out = 0 and lse = -inf.
  * Supported: d_v = 512 (else SMLA_ERR_UNSUPPORTED), num_splits >= 1,
  * rows * num_heads < 2^31; part_out and out 16-byte aligned (else
  * SMLA_ERR_INVALID_ARG).  Asynchronous on `stream`; allocates nothing.
  */
-smla_status_t smla_combine(const float *part_out, const float *part_lse, int32_t num_splits, int32_t rows,
+smla_status_t smla_combine(const void *part_out, const float *part_lse, int32_t num_splits, int32_t rows,
                            int32_t num_heads, int32_t d_v, void *out, float *lse, void *stream);
 
 /*

@@ -146,16 +146,17 @@ def decode_partial(plan: Plan, q, kv_cache, block_table, indices, seq_lens, soft
 
 
 def workspace_parts(plan: Plan, workspace):
-    """Views (part_out [S, rows, H, d_v], part_lse [S, rows, H]) of a split plan's workspace."""
+    """Views (part_out bf16 [S, rows, H, d_v], part_lse fp32 [S, rows, H]) of a split plan's workspace."""
     import torch
     S, rows, H, dv = plan.num_splits, plan.rows, plan.prob.num_heads, plan.prob.d_v
     n_out = S * rows * H * dv
-    f = workspace.view(torch.float32)
-    return f[:n_out].view(S, rows, H, dv), f[n_out:n_out + S * rows * H].view(S, rows, H)
+    po = workspace[: 2 * n_out].view(torch.bfloat16).view(S, rows, H, dv)
+    pl = workspace[2 * n_out: 2 * n_out + 4 * S * rows * H].view(torch.float32).view(S, rows, H)
+    return po, pl
 
 
 def combine(part_out, part_lse, out, lse, stream=None) -> None:
-    """Enqueue smla_combine: part_out [S, rows, H, d_v] fp32, part_lse [S, rows, H] fp32."""
+    """Enqueue smla_combine: part_out [S, rows, H, d_v] bf16, part_lse [S, rows, H] fp32."""
     S, rows, H, d_v = part_out.shape
     _check(load().smla_combine(_ptr(part_out), _ptr(part_lse), S, rows, H, d_v, _ptr(out), _ptr(lse),
                                _stream(stream)),

@@ -8,15 +8,15 @@
 //   M = max_i lse_i;  lse = M + ln sum_i exp(lse_i - M);
 //   out = sum_i exp(lse_i - lse) * part_out_i  (parts with lse_i = -inf are
 //   ignored, whatever their part_out holds),
-// accumulated in fp32 and rounded to bf16 at the store.  A pair whose parts
+// (part_out in bf16) accumulated in fp32 and rounded to bf16 at the store.  A pair whose parts
 // are all empty gets out = 0 and lse = -inf.
 //
 // One to four waves per pair.  The weights of all parts are computed with
 // lane i holding part i (then i + 64, ...) and wave-wide max / sum reductions;
-// the output loop then streams the parts' rows with 16-byte loads, lane l
-// owning 8 consecutive value dims, in batches of 16, 8, 4 or 1 parts (fitting
-// S exactly) whose loads are all issued before any is consumed, so a pair
-// costs about S / 16 memory round trips rather than S.
+// the output loop then streams the parts' bf16 rows with 16-byte loads, lane
+// l owning 8 consecutive value dims, in batches of 16, 8, 4 or 1 parts
+// (fitting S exactly) whose loads are all issued before any is consumed, so a
+// pair costs about S / 16 memory round trips rather than S.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -43,26 +43,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Adds parts s_first .. s_first + NB - 1 (weights in lanes w_lane .. w_lane + NB - 1
-// of `w`) to the accumulators; all 2 * NB loads are issued before any is used.
+// of `w`) to the accumulators; all NB loads are issued before any is used.
 template <int NB>
-__device__ __forceinline__ void add_parts(const float* base, int64_t part_stride, int s_first, int w_lane, float w,
+__device__ __forceinline__ void add_parts(const uint16_t* base, int64_t part_stride, int s_first, int w_lane, float w,
                                           f32x4& acc0, f32x4& acc1) {
-    f32x4 v0[NB], v1[NB];
+    bf16x8 v[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const float* p = base + (int64_t)(s_first + j) * part_stride;
-        v0[j] = *(const f32x4*)p;
-        v1[j] = *(const f32x4*)(p + 4);
-    }
+    for (int j = 0; j < NB; ++j) v[j] = *(const bf16x8*)(base + (int64_t)(s_first + j) * part_stride);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), w_lane + j));
         // a select, not a branch, so the loads stay batched; an ignored part
         // (weight 0) adds nothing, not even a NaN
         const bool use = wj != 0.f;
-        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc0 += wj * (use ? v0[j] : zero);
-        acc1 += wj * (use ? v1[j] : zero);
+        f32x4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x0[e] = use ? (float)v[j][e] : 0.f;
+            x1[e] = use ? (float)v[j][4 + e] : 0.f;
+        }
+        acc0 += wj * x0;
+        acc1 += wj * x1;
     }
 }
 
@@ -71,7 +72,7 @@ __device__ __forceinline__ void add_parts(const float* base, int64_t part_stride
 // waves 1..NW-1 hand their sums to wave 0 through LDS.  Several waves per pair
 // put more loads in flight when there are few pairs (small batch).
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void combine_kernel(const float* __restrict__ part_out,
+__global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __restrict__ part_out,
                                                           const float* __restrict__ part_lse, int num_splits,
                                                           int64_t pairs, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const float* __restric
     if (total != -INFINITY) {
         const int per_w = (num_splits + NW - 1) / NW;
         const int lo = min(num_splits, w * per_w), hi = min(num_splits, lo + per_w);
-        const float* base = part_out + pair * kDv + 8 * lane;
+        const uint16_t* base = part_out + pair * kDv + 8 * lane;
         const int64_t part_stride = pairs * kDv;
         for (int s0 = lo; s0 < hi; s0 += 64) {
             // weight of part s0 + lane (0 for an empty part or past the range)
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const float* __restric
 
 }  // namespace
 
-smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
+smla_status_t launch_combine(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs,
                              void* out, float* lse, hipStream_t stream) {
     if (pairs == 0) return SMLA_OK;
     // few pairs (small batch): four waves per pair so that more part loads are in flight
@@ -155,7 +156,7 @@ smla_status_t launch_combine(const float* part_out, const float* part_lse, int n
 
 }  // namespace smla
 
-extern "C" smla_status_t smla_combine(const float* part_out, const float* part_lse, int32_t num_splits,
+extern "C" smla_status_t smla_combine(const void* part_out, const float* part_lse, int32_t num_splits,
                                       int32_t rows, int32_t num_heads, int32_t d_v, void* out, float* lse,
                                       void* stream) {
     if (num_splits < 1 || rows < 0 || num_heads < 0 || d_v <= 0) return SMLA_ERR_INVALID_ARG;
@@ -166,5 +167,5 @@ extern "C" smla_status_t smla_combine(const float* part_out, const float* part_l
     if (!part_out || !part_lse || !out || !lse) return SMLA_ERR_INVALID_ARG;
     if (((uintptr_t)part_out & 15) != 0 || ((uintptr_t)out & 15) != 0) return SMLA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return smla::launch_combine(part_out, part_lse, num_splits, pairs, out, lse, (hipStream_t)stream);
+    return smla::launch_combine((const uint16_t*)part_out, part_lse, num_splits, pairs, out, lse, (hipStream_t)stream);
 }

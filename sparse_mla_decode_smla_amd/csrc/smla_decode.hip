@@ -41,7 +41,7 @@
 
 namespace smla {
 
-smla_status_t launch_combine(const float* part_out, const float* part_lse, int num_splits, int64_t pairs,
+smla_status_t launch_combine(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs,
                              void* out, float* lse, hipStream_t stream);
 
 namespace {
@@ -70,7 +70,7 @@ struct PartialArgs {
     const int32_t* seq_lens;
     uint16_t* out;
     float* lse;
-    float* part_out;
+    uint16_t* part_out;  // bf16 partial outputs [S, rows, H, d_v]
     float* part_lse;
     int64_t num_kv_blocks;
     int32_t rows, q_len, topk, max_blocks, tokens_per_split, num_splits;
@@ -264,21 +264,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int h = 32 * half + hl;
             const f32x4 x0 = lds_load<f32x4>(lds + hl * kRowPitch + 16 * lane);
             const f32x4 x1 = lds_load<f32x4>(lds + hl * kRowPitch + 1024 + 16 * lane);
+            bf16x4 v0, v1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v0[e] = (__bf16)x0[e];
+                v1[e] = (__bf16)x1[e];
+            }
             if (a.num_splits == 1) {
                 uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 4 * lane;
-                bf16x4 v0, v1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v0[e] = (__bf16)x0[e];
-                    v1[e] = (__bf16)x1[e];
-                }
                 *(bf16x4*)o = v0;
                 *(bf16x4*)(o + 256) = v1;
             } else {
-                // (streaming stores: the partials are read once, by the combine kernel)
-                float* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 4 * lane;
-                __builtin_nontemporal_store(x0, (f32x4*)o);
-                __builtin_nontemporal_store(x1, (f32x4*)(o + 256));
+                // bf16 partials (rounded once more than the output; the combine adds
+                // them in fp32); streaming stores: they are read once, by the combine
+                uint16_t* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 4 * lane;
+                __builtin_nontemporal_store(__builtin_bit_cast(i32x2, v0), (i32x2*)o);
+                __builtin_nontemporal_store(__builtin_bit_cast(i32x2, v1), (i32x2*)(o + 256));
             }
         }
     };
@@ -929,8 +930,8 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
     args.lse = lse;
     const int S = plan->num_splits;
     const int64_t pairs = (int64_t)plan->rows * kHeads;
-    args.part_out = S > 1 ? (float*)workspace : nullptr;
-    args.part_lse = S > 1 ? (float*)workspace + (size_t)S * pairs * kDv : nullptr;
+    args.part_out = S > 1 ? (uint16_t*)workspace : nullptr;
+    args.part_lse = S > 1 ? (float*)((uint16_t*)workspace + (size_t)S * pairs * kDv) : nullptr;
     args.num_kv_blocks = num_kv_blocks;
     args.rows = plan->rows;
     args.q_len = plan->prob.q_len;

@@ -213,10 +213,17 @@ def test_combine_kernel_alone(S):
         pl[1, 0, :] = -np.inf
         po[1, 0, :, :] = np.nan                 # an empty part's values are ignored
     pl[:, 2, 5] = -np.inf                       # every part of one pair empty
-    ref_o, ref_l = oracle.lse_combine(np.nan_to_num(po).astype(np.float64), pl.astype(np.float64))
+    # the partial outputs are bf16: the oracle merges exactly the same (decoded) values
+    po_bits = I.bf16_bits_rne(np.nan_to_num(po))
+    if S > 1:
+        po_bits[1, 0, :, :] = 0x7FC0            # bf16 NaN
+    po_ref = oracle_pins.np_bf16(po_bits)
+    po_ref[np.isnan(po_ref)] = 0.0
+    ref_o, ref_l = oracle.lse_combine(po_ref, pl.astype(np.float64))
     out = torch.empty((rows, H, dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((rows, H), dtype=torch.float32, device="cuda")
-    B().combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, lse)
+    po_dev = torch.from_numpy(po_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    B().combine(po_dev, torch.from_numpy(pl).cuda(), out, lse)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     lg = lse.cpu().numpy()
