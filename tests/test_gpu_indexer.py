@@ -179,3 +179,31 @@ def test_indexer_feeds_decode():
     lerr = float(np.abs(lse.cpu().numpy() - ref_l).max())
     note(f"  indexer -> decode: out err {err:.3e}, lse err {lerr:.3e}")
     assert err <= 2e-2 and err <= 1e-2 * np.abs(ref_o).max() and lerr <= 1e-3
+
+
+def test_indexer_graph_capture_replays():
+    """smla_indexer_topk captured once and replayed with new queries written in place between replays."""
+    inp = I.small_indexer_inputs(batch=3, q_len=2, topk=150, seq_len_range=(200, 900), seed=38)
+    q, k, bt, sl = B().indexer_to_device(inp)
+    mb = bt.shape[1]
+    ws = torch.empty(B().indexer_workspace_size(3, 2, mb), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((3, 2, 150), dtype=torch.int32, device="cuda")
+    sc = torch.empty((3, 2, 150), dtype=torch.float32, device="cuda")
+    B().indexer_topk(q, k, bt, sl, 150, out_indices=idx, out_scores=sc, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            B().indexer_topk(q, k, bt, sl, 150, out_indices=idx, out_scores=sc, workspace=ws, stream=stream)
+    rng = np.random.default_rng(39)
+    for rep in range(3):
+        new_q = I.bf16_bits_rne(rng.standard_normal(inp.q_idx.shape).astype(np.float32))
+        q.copy_(torch.from_numpy(new_q.view(np.int16)).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        inp_r = I.IndexerInputs(workload=inp.workload, q_idx=new_q, k_cache=inp.k_cache,
+                                block_table=inp.block_table, seq_lens=inp.seq_lens)
+        ws_scores = ws[: 3 * 2 * 64 * mb * 4].view(torch.float32).view(3, 2, 64 * mb)
+        check(inp_r, 150, idx.cpu().numpy(), sc.cpu().numpy(), ws_scores.cpu().numpy(), f"indexer graph replay {rep}")

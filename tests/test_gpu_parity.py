@@ -344,3 +344,35 @@ def test_workload_parity_sampled_rows(w):
         inp.q[bsel], inp.kv_cache, inp.block_table[bsel], inp.indices[bsel], inp.seq_lens[bsel],
         inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format, block_size=w.block_size, threads=16)
     check(out[bsel], lse[bsel], ref_o, ref_l, f"{w.name} sequences {bsel}")
+
+
+def test_graph_capture_replays_v4():
+    """The pages' layout: run (partial + combine) captured once, replayed with new lists and queries."""
+    inp = I.small_inputs(batch=2, q_len=2, topk=192, seq_len=1024, kv_format=I.KV_FP8_NOPE_UE8M0, seed=97)
+    w = inp.workload
+    q, kv, bt, idx, sl = B().to_device(inp)
+    plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, d_qk=w.d_qk,
+                           force_splits=3)
+    out = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device="cuda")
+    ws = B().alloc_workspace(plan, "cuda")
+    stream = torch.cuda.Stream()
+    B().decode_run(plan, q, kv, bt, idx, sl, inp.softmax_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            B().decode_run(plan, q, kv, bt, idx, sl, inp.softmax_scale, out, lse, ws, stream=stream)
+    rng = np.random.default_rng(98)
+    for rep in range(3):
+        new_idx = np.stack([rng.permutation(1024)[:192] for _ in range(4)]).astype(np.int32).reshape(2, 2, 192)
+        new_idx[1, 1, rng.choice(192, size=30, replace=False)] = -1
+        new_q = I.bf16_bits_rne(rng.standard_normal(inp.q.shape).astype(np.float32)).astype(np.uint16)
+        idx.copy_(torch.from_numpy(new_idx))
+        q.copy_(torch.from_numpy(new_q.view(np.int16)).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        inp_r = I.Inputs(**{**inp.__dict__, "q": new_q, "indices": new_idx})
+        ref_o, ref_l = oracle.decode_inputs(inp_r)
+        check(out, lse, ref_o, ref_l, f"v4 graph replay {rep}")
