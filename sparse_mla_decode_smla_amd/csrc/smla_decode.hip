@@ -201,49 +201,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ntiles = (nk + kTile - 1) / kTile;
 
     // ---- logical positions -> physical rows (masked entries -> -1), by the PV
-    // waves (threads 256..511) while the QK waves load Q.  When the
-    // sequence's block-table row is short, it is first copied into the (still
-    // empty) stage ring together with the index list, so each entry costs one
-    // LDS lookup instead of a second dependent global load.  Barriers T1 (copy
-    // done) and B0 (row table done) are run by every wave.
+    // waves (threads 256..511) while the QK waves load Q.  The index list
+    // goes into the row table, and (when the sequence's block-table row is
+    // short) the block-table row into the still empty stage ring, by LDS-DMA:
+    // every copy instruction is issued before the one wait, so the copy costs
+    // one memory round trip, not one per 256 entries.  Each entry then costs
+    // one LDS lookup.  Barriers T1 (copies done) and B0 (row table done) are
+    // run by every wave.
     auto build_row_table = [&]() {
         const int pt = tid - 4 * 64;  // 0..255
-        int64_t cap = (int64_t)kBlock * a.max_blocks;
-        if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
+        const int pw = pt >> 6;       // PV wave 0..3
         const int32_t* idx = a.indices + (int64_t)r * a.topk + k0;
         const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
         const int nent = ntiles * kTile;
         constexpr int kMaxBtInLds = 4096;
         static_assert(kMaxBtInLds * 4 <= NST * STAGE, "block-table copy exceeds the stage ring");
-        if (a.max_blocks <= kMaxBtInLds) {
-            __attribute__((address_space(3))) int* btl = (__attribute__((address_space(3))) int*)lds;
-            for (int i = pt; i < a.max_blocks; i += 256) btl[i] = bt[i];
-            for (int i = pt; i < nent; i += 256)
-                *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = i < nk ? idx[i] : -1;
-            __syncthreads();  // T1
+        const bool bt_in_lds = a.max_blocks <= kMaxBtInLds;
+        // 64-entry chunks, chunk c by PV wave c % 4; lane l copies entry 64c + l
+        // (lanes past the end copy nothing; index-list entries past nk are -1)
+        if (bt_in_lds)
+            for (int c = pw; 64 * c < a.max_blocks; c += 4)
+                if (64 * c + lane < a.max_blocks) lds_dma4(bt + 64 * c + lane, lds0 + 256u * c);
+        const unsigned rt0 = (unsigned)(uintptr_t)rowtab;
+        for (int c = pw; 64 * c < nent; c += 4) {
+            const int i = 64 * c + lane;
+            if (i < nk)
+                lds_dma4(idx + i, rt0 + 256u * c);
+            else if (i < nent)
+                *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = -1;
+        }
+        // (read after the copies are issued: the compiler waits for this load
+        // where it is made, and it would otherwise delay them by a round trip)
+        int64_t cap = (int64_t)kBlock * a.max_blocks;
+        if (a.seq_lens) cap = min(cap, (int64_t)a.seq_lens[b]);
+        wait_vmcnt<0>();
+        __syncthreads();  // T1
+        __attribute__((address_space(3))) int* const rt = (__attribute__((address_space(3))) int*)rowtab;
+        if (bt_in_lds) {
+            const __attribute__((address_space(3))) int* btl = (const __attribute__((address_space(3))) int*)lds;
             for (int i = pt; i < nent; i += 256) {
-                __attribute__((address_space(3))) int* e = (__attribute__((address_space(3))) int*)(rowtab + 4 * i);
-                const int pos = *e;
+                const int pos = rt[i];
                 int row = -1;
                 if (pos >= 0 && (int64_t)pos < cap) {
                     const int blk = btl[pos / kBlock];
                     if (blk >= 0 && (int64_t)blk < a.num_kv_blocks) row = blk * kBlock + (pos % kBlock);
                 }
-                *e = row;
+                rt[i] = row;
             }
         } else {
-            for (int i = pt; i < nent; i += 256) {
-                int row = -1;
-                if (i < nk) {
-                    const int pos = idx[i];
-                    if (pos >= 0 && (int64_t)pos < cap) {
-                        const int blk = bt[pos / kBlock];
-                        if (blk >= 0 && (int64_t)blk < a.num_kv_blocks) row = blk * kBlock + (pos % kBlock);
-                    }
+            // long block-table row: 8 lookups in flight per lane (an entry
+            // out of range reads entry 0 and discards it)
+            for (int i0 = pt; i0 < nent; i0 += 8 * 256) {
+                int pos[8], blk[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = i0 + 256 * j;
+                    pos[j] = i < nent ? rt[i] : -1;
+                    if (!(pos[j] >= 0 && (int64_t)pos[j] < cap)) pos[j] = -1;
                 }
-                *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = row;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) blk[j] = bt[pos[j] >= 0 ? pos[j] / kBlock : 0];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int i = i0 + 256 * j;
+                    if (i < nent)
+                        rt[i] = pos[j] >= 0 && blk[j] >= 0 && (int64_t)blk[j] < a.num_kv_blocks
+                                    ? blk[j] * kBlock + (pos[j] % kBlock)
+                                    : -1;
+                }
             }
-            __syncthreads();  // T1
         }
     };
 

@@ -115,6 +115,29 @@ def test_seq_lens_optional(fmt):
     check(out2, lse2, ref_o2, ref_l2, "without seq_lens")
 
 
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+def test_long_block_table_rows(fmt):
+    """Contexts past 4096 blocks of 64 tokens: the block-table row is too long to
+    be staged in LDS, so each position's block is looked up in global memory."""
+    d_qk = 512 if fmt == I.KV_FP8_NOPE_UE8M0 else 576
+    w = I.Workload(f"long_b2_topk200_{FMT_IDS[fmt]}", batch=2, q_len=1, topk=200, kv_format=fmt, paged=True,
+                   seq_len_range=(270_000, 300_000), d_qk=d_qk, d_v=512)
+    inp = I.make_inputs(w, seed=41 + fmt, fill="selected")
+    assert inp.block_table.shape[1] > 4096
+    idx = inp.indices.copy()
+    idx[0, 0, 5] = int(inp.seq_lens[0]) + 3      # past seq_lens, inside the table: masked
+    idx[1, 0, 7] = -1
+    bt = inp.block_table.copy()
+    bt[1, int(idx[1, 0, 9]) // 64] = -2          # a bad block id masks its positions
+    note(f"long block table fmt={fmt} max_blocks={bt.shape[1]} seq_lens={inp.seq_lens.tolist()}")
+    ref_o, ref_l = oracle.default().sparse_mla_decode(inp.q, inp.kv_cache, bt, idx, inp.seq_lens,
+                                                      inp.softmax_scale, d_v=w.d_v, kv_format=fmt,
+                                                      block_size=64, threads=8)
+    for splits in (0, 3):
+        out, lse = run_gpu(inp, indices=idx, force_splits=splits, block_table=bt)
+        check(out, lse, ref_o, ref_l, f"long table fmt{fmt} S{splits}")
+
+
 @pytest.mark.parametrize("fmt", FORMATS[:2], ids=FMT_IDS[:2])
 def test_late_large_scores_restart(fmt):
     # A token near the end of each list gets a score far above the first tiles' max
