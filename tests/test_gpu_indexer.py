@@ -145,6 +145,33 @@ def test_indexer_rows_longer_than_registers():
     check(inp, 300, idx, sc, ws, "long rows")
 
 
+@pytest.mark.parametrize("seq_len_range", [(9000, 16000), (20000, 32000)], ids=["per16", "per32"])
+def test_indexer_register_sizes(seq_len_range):
+    # rows of up to 16384 and 32768 positions: 16 and 32 keys per select thread
+    inp = I.small_indexer_inputs(batch=2, q_len=2, topk=2048, seq_len_range=seq_len_range, seed=42)
+    note(f"indexer rows {seq_len_range}: seq_lens {inp.seq_lens.tolist()}")
+    idx, sc, ws = run_indexer(inp, 2048)
+    check(inp, 2048, idx, sc, ws, f"rows {seq_len_range}")
+
+
+@pytest.mark.parametrize("seq_len", [2000, 40000])
+def test_indexer_one_outlier_key(seq_len):
+    # one key equal to 64 q: its score is far above all others, so the keys
+    # near the row's largest are fewer than the list needs and the selection
+    # counts the rest as well
+    inp = I.small_indexer_inputs(batch=2, q_len=1, topk=300, seq_len=seq_len, seed=43)
+    k2 = inp.k_cache.copy()
+    p0 = seq_len // 3
+    q = inp.q_idx[0, 0].view(np.uint16).astype(np.uint32) << 16
+    big = (q.view(np.float32) * np.float32(64.0)).view(np.uint32) >> 16      # exact: a power of two
+    k2.reshape(-1, 128)[inp.block_table[0, p0 // 64] * 64 + p0 % 64] = big.astype(np.uint16)
+    inp2 = I.IndexerInputs(workload=inp.workload, q_idx=inp.q_idx, k_cache=k2, block_table=inp.block_table,
+                           seq_lens=inp.seq_lens)
+    idx, sc, ws = run_indexer(inp2, 300)
+    assert p0 in idx[0, 0]
+    check(inp2, 300, idx, sc, ws, f"outlier n={seq_len}")
+
+
 @pytest.mark.parametrize("name", [w.name for w in I.INDEXER_WORKLOADS])
 def test_indexer_workloads(name):
     w = I.INDEXER_WORKLOADS_BY_NAME[name]
