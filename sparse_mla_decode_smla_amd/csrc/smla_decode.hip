@@ -3,8 +3,10 @@
 //
 // One workgroup handles one query row (b, s), all 64 heads, and one part of
 // that row's top-k list.  Every selected latent row is gathered from the
-// paged cache into LDS once and read from there by all four waves (wave w
-// owns heads [16w, 16w + 16)): the head batching of "The MMA Sparse-MLA
+// paged cache into LDS once and read from there by all eight waves: QK
+// waves 0..3 (wave w owns heads [16w, 16w + 16)) and PV waves 4..7 (wave
+// 4 + p owns value dims [128p, 128p + 128) and issues a quarter of the
+// gathers).  This is the head batching of "The MMA Sparse-MLA
 // Decode Kernel: A Deep Dive into AI Inference Optimization on Blackwell
 // GPUs" (Agent Reasoning, "Design Decisions" 1 and "Memory Budgeting"), here
 // with all 64 heads in one workgroup since a gfx950 CU has 160 KB of LDS.
