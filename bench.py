@@ -32,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -59,11 +60,20 @@ def is_indexer(workload: str) -> bool:
     return workload.startswith("idx_")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed (the
+    sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(workload: str = DEFAULT_WORKLOAD) -> str:
+    """Hash of the code of the kernel sources (comments and layout do not count)."""
     h = hashlib.sha256()
     for f in (INDEXER_SOURCES if is_indexer(workload) else KERNEL_SOURCES):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
