@@ -138,8 +138,9 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
     kernel = SCORE_KERNEL if is_indexer(workload) else PARTIAL_KERNEL
     fetch_kib, nf = _counter_means(fetch_dir, "FETCH_SIZE", kernel)
     write_kib, nw = _counter_means(write_dir, "WRITE_SIZE", kernel)
-    cf_kib, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "elementwise")
-    cw_kib, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "elementwise")
+    # the probe's own dispatches only (not the fill that creates its input)
+    cf_kib, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "bitwise_not")
+    cw_kib, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "bitwise_not")
     f_scale = COPY_PROBE_BYTES / (cf_kib * 1024.0)
     w_scale = COPY_PROBE_BYTES / (cw_kib * 1024.0)
     fetch_b = fetch_kib * 1024.0 * f_scale
