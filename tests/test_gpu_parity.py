@@ -138,6 +138,22 @@ def test_long_block_table_rows(fmt):
         check(out, lse, ref_o, ref_l, f"long table fmt{fmt} S{splits}")
 
 
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+def test_part_at_the_row_table_cap(fmt):
+    """A part as long as the LDS row table allows, then a short one (a single
+    part was asked for; the plan splits the list at the cap)."""
+    d_qk = 512 if fmt == I.KV_FP8_NOPE_UE8M0 else 576
+    cap = B().decode_plan(1, 1, 16384, 1, fmt, d_qk=d_qk, force_splits=1).tokens_per_split
+    topk = cap + 96
+    plan = B().decode_plan(1, 1, topk, (topk + 600 + 63) // 64, fmt, d_qk=d_qk, force_splits=1)
+    assert (plan.num_splits, plan.tokens_per_split) == (2, cap)
+    inp = I.small_inputs(batch=1, q_len=1, topk=topk, seq_len=topk + 600, kv_format=fmt, seed=51 + fmt)
+    note(f"row-table cap fmt={fmt}: part of {cap} tokens, top-k {topk}")
+    ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
+    out, lse = run_gpu(inp, force_splits=1)
+    check(out, lse, ref_o, ref_l, f"cap fmt{fmt}")
+
+
 @pytest.mark.parametrize("fmt", FORMATS[:2], ids=FMT_IDS[:2])
 def test_late_large_scores_restart(fmt):
     # A token near the end of each list gets a score far above the first tiles' max
