@@ -71,6 +71,9 @@ __device__ __forceinline__ float key_score(unsigned k) {
 }
 
 // grid (ceil(max_blocks / (kScoreWaves * kBlocksPerWave)), batch), 256 threads.
+// QL >= q_len query rows are held in registers: one row needs 76 VGPRs (six
+// waves per SIMD), four need 137 (three).
+template <int QL>
 __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t* __restrict__ q_idx,
                                                                   const uint8_t* __restrict__ k_cache,
                                                                   int64_t num_kv_blocks,
@@ -87,9 +90,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
     const int64_t row0 = (int64_t)b * q_len;
 
     // this lane's 8 query dims of each row of the sequence
-    bf16x2 qv[kMaxQlen][4];
+    bf16x2 qv[QL][4];
 #pragma unroll
-    for (int s = 0; s < kMaxQlen; ++s) {
+    for (int s = 0; s < QL; ++s) {
         if (s < q_len) {
             const u32x4 v = *(const u32x4*)(q_idx + (row0 + s) * kDidx + 8 * c);
             // (each element goes through a scalar: bit-casting a vector element in
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
 #pragma unroll
         for (int t = 0; t < 16; ++t) kv[t] = __builtin_nontemporal_load((const u32x4*)(base + (4 * t + g) * (2 * kDidx)));
 #pragma unroll
-        for (int s = 0; s < kMaxQlen; ++s) {
+        for (int s = 0; s < QL; ++s) {
             if (s >= q_len) break;
             float mine = 0.f;
 #pragma unroll
@@ -416,9 +419,18 @@ smla_status_t launch_scores(const void* q_idx, const void* k_cache, int64_t num_
                             int32_t max_blocks_per_seq, float* scores, hipStream_t st) {
     const int per_wg = kScoreWaves * kBlocksPerWave;
     dim3 g1((unsigned)((max_blocks_per_seq + per_wg - 1) / per_wg), (unsigned)batch);
-    hipLaunchKernelGGL(score_kernel, g1, dim3(64 * kScoreWaves), 0, st, (const uint16_t*)q_idx,
-                       (const uint8_t*)k_cache, num_kv_blocks, block_table, seq_lens, (int)q_len,
-                       (int)max_blocks_per_seq, scores);
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, g1, dim3(64 * kScoreWaves), 0, st, (const uint16_t*)q_idx,
+                           (const uint8_t*)k_cache, num_kv_blocks, block_table, seq_lens, (int)q_len,
+                           (int)max_blocks_per_seq, scores);
+    };
+    static_assert(kMaxQlen == 4, "the score kernel is instantiated for up to four query rows");
+    if (q_len == 1)
+        launch(score_kernel<1>);
+    else if (q_len == 2)
+        launch(score_kernel<2>);
+    else
+        launch(score_kernel<4>);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
