@@ -6,6 +6,7 @@ max |lse - ref| <= 1e-3; rows with no valid index must give out = 0 and
 lse = -inf exactly.  Index handling is exact by construction (the same
 bytes go to both sides).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -152,6 +153,36 @@ def test_part_at_the_row_table_cap(fmt):
     ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
     out, lse = run_gpu(inp, force_splits=1)
     check(out, lse, ref_o, ref_l, f"cap fmt{fmt}")
+
+
+def _bf16_times_pow2(bits, factor):
+    """bf16 bit patterns times a power of two (exact while the result stays in range)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+def test_query_magnitudes(fmt):
+    """Queries far from unit size, a zero head, outliers and groups of very different size in one head.
+    (The fp8-cache path splits each 128-group of Q into two e4m3 halves under a power-of-two prescale;
+    these cases reach the prescale's range and the low half's.)"""
+    base = I.small_inputs(batch=2, q_len=1, topk=200, seq_len=700, kv_format=fmt, seed=41 + fmt)
+    cases = []
+    for k in (-30, 30):  # Q * 2^k with the softmax scale * 2^-k: the same scores
+        scale = float(np.float32(base.softmax_scale) * np.float32(2.0 ** -k))
+        cases.append((f"Q*2^{k}", dataclasses.replace(base, q=_bf16_times_pow2(base.q, 2.0 ** k),
+                                                      softmax_scale=scale)))
+    q = base.q.copy()
+    q[:, :, 5, :] = 0                                                   # a zero head
+    q[:, :, 6, 0:448:64] = _bf16_times_pow2(np.full_like(q[:, :, 6, 0:448:64], 0x3F80), 32.0)  # outliers 32
+    q[:, :, 7, 128:384] = _bf16_times_pow2(q[:, :, 7, 128:384], 2.0 ** -12)   # two small groups
+    q[:, :, 8, :] = _bf16_times_pow2(q[:, :, 8, :], 2.0 ** -100)               # a tiny head
+    cases.append(("mixed heads", dataclasses.replace(base, q=q)))
+    for what, inp in cases:
+        note(f"query magnitudes fmt={fmt}: {what}")
+        ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
+        out, lse = run_gpu(inp)
+        check(out, lse, ref_o, ref_l, f"fmt{fmt} {what}")
 
 
 @pytest.mark.parametrize("fmt", FORMATS[:2], ids=FMT_IDS[:2])
