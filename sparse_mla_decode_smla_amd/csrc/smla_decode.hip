@@ -19,12 +19,10 @@
 //   gather  : 16-byte LDS-DMA loads (global_load_lds_dwordx4) of whole rows,
 //             pipelined over a ring of LDS stages; masked tokens load zeros;
 //   QK^T    : S^T[token, head] = K . Q^T with v_mfma_f32_16x16x32_bf16,
-//             Q held in registers, K read from LDS.  fp8 rows: the cached
-//             e4m3 codes go into the fp8 MFMA (16x16x128) as they are,
-//             against Q split exactly into two e4m3 halves; the per-128 fp32
-//             scale multiplies each group's partial scores.  The pages'
-//             layout: e4m3 widened to bf16 in registers, the power-of-two
-//             UE8M0 scales applied exactly inside the widening;
+//             Q held in registers, K read from LDS (fp8 rows are widened to
+//             bf16 in registers; the per-128 fp32 scale multiplies the
+//             per-group partial scores; the power-of-two UE8M0 scales of the
+//             pages' layout are applied exactly inside the widening);
 //   softmax : online, base 2, running max and sum per head in registers,
 //             masked tokens get -inf ("Edge Case Handling": invalid tokens
 //             never enter the softmax);
@@ -56,7 +54,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -119,15 +116,6 @@ __device__ __forceinline__ int swz4(int t) { return (t >> 2) & 3; }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16x16x128 e4m3 x e4m3 product, fp32 accumulation; B's codes are taken
-// times 2^(sb - 127) (an E8M0 block scale; here the same for all of a
-// column's k-blocks), A's times 1.  Each lane's 32 codes of A and of B pair up
-// byte for byte, so any assignment of the 128 k-values to (lane group, byte)
-// that A and B share gives the same sum.
-__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c, int sb) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 template <typename T>
@@ -433,57 +421,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
 
-        // fp8 rows: per 128-group, the c_kv dims of Q become two e4m3 halves
-        // hi + lo / 16 = Q * 2^qe exactly, so that QK runs on the fp8 MFMA over
-        // the cached codes as they are, with no widening.  A bf16 value has 8
-        // significant bits; hi keeps the leading 4 and the remainder, times 16,
-        // needs at most 4 more.  qe puts the group's largest |Q| of the head in
-        // [128, 256) (e4m3 reaches 448); the MFMA's B block scale takes back
-        // 2^-qe (hi) and 2^-(qe + 4) (lo) exactly.  Both halves are exact for
-        // every |Q| down to 2^-14 of the group's largest; below that the error
-        // stays under 2^-21 of it.  Lane (head, g) holds, per 128-group, the
-        // dims of the two 16-byte chunks g and 4 + g of the group's band: the
-        // chunks that the K operand of the lane's token reads.
-        constexpr int NG8 = FMT == 1 ? 4 : 1;  // fp8 products per token block
-        i32x8 qhi[NG8], qlo[NG8];
-        int sbh[NG8], sbl[NG8];  // E8M0 block scales of the hi and lo products
-        if (FMT == 1) {
-#pragma unroll
-            for (int grp = 0; grp < NG8; ++grp) {
-                float mq = 0.f;
-#pragma unroll
-                for (int hf = 0; hf < 4; ++hf)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf((float)qreg[4 * grp + hf][e]));
-                mq = fmaxf(mq, __shfl_xor(mq, 16));
-                mq = fmaxf(mq, __shfl_xor(mq, 32));
-                int ex = 0;
-                (void)frexpf(mq, &ex);  // mq = f * 2^ex, f in [0.5, 1)
-                const int qe = mq > 0.f ? min(100, max(-100, 8 - ex)) : 0;
-                const float up = ldexpf(1.f, qe);
-                sbh[grp] = 127 - qe;
-                sbl[grp] = 127 - qe - 4;
-#pragma unroll
-                for (int hf = 0; hf < 4; ++hf)  // 8 dims of run 4 grp + hf (dwords 2 hf, 2 hf + 1)
-#pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        const bf16x8 v = qreg[4 * grp + hf];
-                        const float x0 = (float)v[4 * w] * up, x1 = (float)v[4 * w + 1] * up;
-                        const float x2 = (float)v[4 * w + 2] * up, x3 = (float)v[4 * w + 3] * up;
-                        int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-                        h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
-                        const float r0 = (x0 - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.f;
-                        const float r1 = (x1 - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.f;
-                        const float r2 = (x2 - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.f;
-                        const float r3 = (x3 - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.f;
-                        int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-                        l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
-                        qhi[grp][2 * hf + w] = h;
-                        qlo[grp][2 * hf + w] = l;
-                    }
-            }
-        }
-
         // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
         // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
         const int tokA0 = i16, tokA1 = 16 + i16;
@@ -601,52 +538,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         }
                     }
                 } else {
-                    // rope k-steps 16, 17 (bf16 MFMA), then per 128-group the group's
-                    // 128 codes of each token (chunks g and 4 + g of the group's
-                    // band) times each Q half on the fp8 MFMA; the group's partial
-                    // score takes the token's fp32 scale of that group
-                    const lds_u8* scl = st + NBANDS * kTile * 128;
-                    u32x4 ga[2][2], gb[2][2];  // [buffer][chunk pair half] of blocks 0 and 1
-                    auto load_grp = [&](int grp, int buf) {
-#pragma unroll
-                        for (int pr = 0; pr < 2; ++pr) {
-                            ga[buf][pr] = lds_load<u32x4>(st + qk0[pr] + grp * kTile * 128);
-                            gb[buf][pr] = lds_load<u32x4>(st + qk1[pr] + grp * kTile * 128);
-                        }
+                    // 10 load units per block: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
+                    constexpr int PF = 3;
+                    u32x4 ka[PF], kb[PF];
+                    auto unit_off = [&](int u, int blk) {
+                        const int* qo = blk == 0 ? qk0 : qk1;
+                        return u < 2 ? qo[u] + 4 * kTile * 128 : qo[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
                     };
-                    const u32x4 ra0 = lds_load<u32x4>(st + qk0[0] + 4 * kTile * 128);
-                    const u32x4 rb0 = lds_load<u32x4>(st + qk1[0] + 4 * kTile * 128);
-                    const u32x4 ra1 = lds_load<u32x4>(st + qk0[1] + 4 * kTile * 128);
-                    const u32x4 rb1 = lds_load<u32x4>(st + qk1[1] + 4 * kTile * 128);
-                    load_grp(0, 0);
+                    const lds_u8* scl = st + NBANDS * kTile * 128;
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
+                        kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         sc0[e] = lds_load<f32x4>(scl + 16 * (tokC0 + e));
                         sc1[e] = lds_load<f32x4>(scl + 16 * (tokC1 + e));
                     }
-                    s0 = mfma16(__builtin_bit_cast(bf16x8, ra0), qreg[16], s0);
-                    s1 = mfma16(__builtin_bit_cast(bf16x8, rb0), qreg[16], s1);
-                    s0 = mfma16(__builtin_bit_cast(bf16x8, ra1), qreg[17], s0);
-                    s1 = mfma16(__builtin_bit_cast(bf16x8, rb1), qreg[17], s1);
+                    f32x4 p0 = s0, p1 = s0;
 #pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        const int bf = grp & 1;
-                        if (grp + 1 < 4) load_grp(grp + 1, bf ^ 1);
-                        const i32x8 A0 = __builtin_bit_cast(
-                            i32x8, __builtin_shufflevector(ga[bf][0], ga[bf][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                        const i32x8 A1 = __builtin_bit_cast(
-                            i32x8, __builtin_shufflevector(gb[bf][0], gb[bf][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-                        f32x4 p0 = mfma_fp8(A0, qhi[grp], z, sbh[grp]);
-                        f32x4 p1 = mfma_fp8(A1, qhi[grp], z, sbh[grp]);
-                        p0 = mfma_fp8(A0, qlo[grp], p0, sbl[grp]);
-                        p1 = mfma_fp8(A1, qlo[grp], p1, sbl[grp]);
+                    for (int u = 0; u < 10; ++u) {
+                        const int sl = u % PF;
+                        if (u < 2) {
+                            s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[16 + u], s0);
+                            s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[16 + u], s1);
+                        } else {
+                            const int grp = (u - 2) >> 1, pr = (u - 2) & 1;
+                            if (pr == 0) { p0 = f32x4{0.f, 0.f, 0.f, 0.f}; p1 = p0; }
+                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][0], ka[sl][1]), qreg[4 * grp + 2 * pr], p0);
+                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][0], kb[sl][1]), qreg[4 * grp + 2 * pr], p1);
+                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][2], ka[sl][3]), qreg[4 * grp + 2 * pr + 1], p0);
+                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][2], kb[sl][3]), qreg[4 * grp + 2 * pr + 1], p1);
+                            if (pr == 1) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            s0[e] += sc0[e][grp] * p0[e];
-                            s1[e] += sc1[e][grp] * p1[e];
+                                for (int e = 0; e < 4; ++e) {
+                                    s0[e] += sc0[e][grp] * p0[e];
+                                    s1[e] += sc1[e][grp] * p1[e];
+                                }
+                            }
+                        }
+                        if (u + PF < 10) {
+                            ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
+                            kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
                         }
                     }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF + 8, 0);
+#pragma unroll
+                    for (int u = 0; u < 10 - PF; ++u) {
+                        if (u < 2)
+                            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        else
+                            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
                 }
 
                 // ---- mask, reference, softmax weights (base 2)

@@ -41,18 +41,14 @@ int query_cu_count(int* out) {
 // to split sweeps of the two kernels on MI355X (256 CUs):
 //   - a workgroup gathers its part at about 30 GB/s per CU, and the whole
 //     launch at most at about 5 TB/s; a 32-token tile costs about 0.9 us of
-//     pipelined compute (bf16 rows), 1.7 us (fp8 rows) or 1.6 us (the
-//     pages' layout); every round of workgroups (one per CU)
+//     pipelined compute (bf16 rows), 1.7 us (fp8 rows, widened in registers)
+//     or 1.6 us (the pages' layout); every round of workgroups (one per CU)
 //     pays about 7.5 us of launch, prologue and epilogue;
 //   - with S > 1 every part writes 64 x 512 bf16 outputs (64 KiB) per row at
 //     about 5 TB/s; the combine kernel pays about 2.3 us, reads them back at
 //     about 8 TB/s, but a (row, head) pair's S rows of 1 KiB come in at no
 //     more than about 40 GB/s per workgroup, and 0.25 us per round of 16 part
 //     loads.
-// (The fp8 figure was fitted while fp8 keys were widened in registers.  The
-// fp8 MFMA path runs a tile in about 1.25 us at low load, but the model with
-// that figure picks fewer parts for short lists, which measured slower: 8
-// query rows of top-k 2048 take 16.5 us with 22 parts, 17.3 with 16.)
 double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus) {
     const double row_bytes = smla::gathered_bytes_per_token(p.kv_format);
     const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.9 : p.kv_format == SMLA_KV_FP8_E4M3_SCALE128 ? 1.7 : 1.6;
