@@ -13,7 +13,9 @@
 //
 // One to four waves per pair.  The weights of all parts are computed with
 // lane i holding part i (then i + 64, ...) and wave-wide max / sum reductions;
-// the output loop then streams the parts' bf16 rows with 16-byte loads, lane
+// with at most 64 parts each lane reads its part's lse once, and that value
+// serves the max, the sum and the weight (a dependent re-read of the lse costs
+// about 0.5 us per call).  The output loop then streams the parts' bf16 rows with 16-byte loads, lane
 // l owning 8 consecutive value dims, in batches of 16, 8, 4 or 1 parts
 // (fitting S exactly) whose loads are all issued before any is consumed, so a
 // pair costs about S / 16 memory round trips rather than S.
@@ -81,39 +83,54 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __rest
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...), in every wave
-    float M = -INFINITY;
-    for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
-    M = wave_max(M);
-    float total = -INFINITY;
-    if (M != -INFINITY) {
-        float z = 0.f;
-        for (int s = lane; s < num_splits; s += 64) {
-            const float l = part_lse[(int64_t)s * pairs + pair];
-            z += l == -INFINITY ? 0.f : expf(l - M);
-        }
-        total = M + logf(wave_sum(z));
-    }
-
+    const int per_w = (num_splits + NW - 1) / NW;
+    const int lo = min(num_splits, w * per_w), hi = min(num_splits, lo + per_w);
+    const uint16_t* base = part_out + pair * kDv + 8 * lane;
+    const int64_t part_stride = pairs * kDv;
     f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    if (total != -INFINITY) {
-        const int per_w = (num_splits + NW - 1) / NW;
-        const int lo = min(num_splits, w * per_w), hi = min(num_splits, lo + per_w);
-        const uint16_t* base = part_out + pair * kDv + 8 * lane;
-        const int64_t part_stride = pairs * kDv;
-        for (int s0 = lo; s0 < hi; s0 += 64) {
-            // weight of part s0 + lane (0 for an empty part or past the range)
-            float wt = 0.f;
-            if (s0 + lane < hi) {
-                const float l = part_lse[(int64_t)(s0 + lane) * pairs + pair];
-                wt = l == -INFINITY ? 0.f : expf(l - total);
-            }
-            const int n = min(64, hi - s0);
+    float total = -INFINITY;
+    if (num_splits <= 64) {
+        // ---- lane s holds part s's lse: one read serves M, the sum and the weights
+        const float l = lane < num_splits ? part_lse[(int64_t)lane * pairs + pair] : -INFINITY;
+        const float M = wave_max(l);
+        if (M != -INFINITY) {
+            total = M + logf(wave_sum(l == -INFINITY ? 0.f : expf(l - M)));
+            const float wt = l == -INFINITY ? 0.f : expf(l - total);  // weight of part `lane`
+            const int n = hi - lo;
             int j0 = 0;
-            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
-            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
-            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
-            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
+            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 8; }
+            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 4; }
+            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
+        }
+    } else {
+        // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...), in every wave
+        float M = -INFINITY;
+        for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
+        M = wave_max(M);
+        if (M != -INFINITY) {
+            float z = 0.f;
+            for (int s = lane; s < num_splits; s += 64) {
+                const float l = part_lse[(int64_t)s * pairs + pair];
+                z += l == -INFINITY ? 0.f : expf(l - M);
+            }
+            total = M + logf(wave_sum(z));
+        }
+        if (total != -INFINITY) {
+            for (int s0 = lo; s0 < hi; s0 += 64) {
+                // weight of part s0 + lane (0 for an empty part or past the range)
+                float wt = 0.f;
+                if (s0 + lane < hi) {
+                    const float l = part_lse[(int64_t)(s0 + lane) * pairs + pair];
+                    wt = l == -INFINITY ? 0.f : expf(l - total);
+                }
+                const int n = min(64, hi - s0);
+                int j0 = 0;
+                for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+                if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
+                if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
+                for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+            }
         }
     }
     if (NW > 1) {
