@@ -52,6 +52,9 @@ __device__ __forceinline__ void add_parts(const uint16_t* base, int64_t part_str
     bf16x8 v[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) v[j] = *(const bf16x8*)(base + (int64_t)(s_first + j) * part_stride);
+    // (the scheduler would otherwise interleave loads and uses of a 16-part
+    // batch, one round trip per part, to keep the kernel under 64 VGPRs)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), w_lane + j));
