@@ -283,6 +283,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // its heads.
     constexpr int kRowPitch = 4 * kDv + 16;
     static_assert(32 * kRowPitch <= NST * STAGE, "staging area exceeds the stage ring");
+    // Output rows of this workgroup: out[r] (one part) or part_out[sp][r].
+    // Both pointers are taken into scalar registers before the choice.  Left
+    // to itself, the compiler chose between the two argument fields' addresses
+    // and read the chosen field with a vector load and a full wait, once per
+    // head stored.
+    uint64_t out_p = (uint64_t)(uintptr_t)a.out, part_p = (uint64_t)(uintptr_t)a.part_out;
+    asm volatile("" : "+s"(out_p), "+s"(part_p));
+    typedef __attribute__((address_space(1))) uint16_t g_u16;
+    g_u16* const obase = a.num_splits == 1 ? (g_u16*)(uintptr_t)out_p + (int64_t)r * kHeads * kDv
+                                           : (g_u16*)(uintptr_t)part_p + ((int64_t)sp * a.rows + r) * kHeads * kDv;
     auto store_half = [&](int half) {
         // wave w stores heads 32*half + 4w .. 32*half + 4w + 3; lane l holds dims
         // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
@@ -298,17 +308,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 v0[e] = (__bf16)x0[e];
                 v1[e] = (__bf16)x1[e];
             }
-            if (a.num_splits == 1) {
-                uint16_t* o = a.out + ((int64_t)r * kHeads + h) * kDv + 4 * lane;
-                *(bf16x4*)o = v0;
-                *(bf16x4*)(o + 256) = v1;
-            } else {
-                // bf16 partials (rounded once more than the output; the combine adds
-                // them in fp32); streaming stores: they are read once, by the combine
-                uint16_t* o = a.part_out + (((int64_t)sp * a.rows + r) * kHeads + h) * kDv + 4 * lane;
-                __builtin_nontemporal_store(__builtin_bit_cast(i32x2, v0), (i32x2*)o);
-                __builtin_nontemporal_store(__builtin_bit_cast(i32x2, v1), (i32x2*)(o + 256));
-            }
+            // (several parts: bf16 partials, rounded once more than the output;
+            // the combine adds them in fp32)
+            typedef __attribute__((address_space(1))) i32x2 g_i32x2;
+            g_u16* o = obase + h * kDv + 4 * lane;
+            *(g_i32x2*)o = __builtin_bit_cast(i32x2, v0);
+            *(g_i32x2*)(o + 256) = __builtin_bit_cast(i32x2, v1);
         }
     };
 
