@@ -288,11 +288,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // to itself, the compiler chose between the two argument fields' addresses
     // and read the chosen field with a vector load and a full wait, once per
     // head stored.
+    // The same for the lse rows.
     uint64_t out_p = (uint64_t)(uintptr_t)a.out, part_p = (uint64_t)(uintptr_t)a.part_out;
-    asm volatile("" : "+s"(out_p), "+s"(part_p));
+    uint64_t lse_p = (uint64_t)(uintptr_t)a.lse, plse_p = (uint64_t)(uintptr_t)a.part_lse;
+    asm volatile("" : "+s"(out_p), "+s"(part_p), "+s"(lse_p), "+s"(plse_p));
     typedef __attribute__((address_space(1))) uint16_t g_u16;
-    g_u16* const obase = a.num_splits == 1 ? (g_u16*)(uintptr_t)out_p + (int64_t)r * kHeads * kDv
-                                           : (g_u16*)(uintptr_t)part_p + ((int64_t)sp * a.rows + r) * kHeads * kDv;
+    typedef __attribute__((address_space(1))) float g_f32;
+    const int64_t orow = a.num_splits == 1 ? (int64_t)r : (int64_t)sp * a.rows + r;
+    g_u16* const obase = (g_u16*)(uintptr_t)(a.num_splits == 1 ? out_p : part_p) + orow * kHeads * kDv;
+    g_f32* const lbase = (g_f32*)(uintptr_t)(a.num_splits == 1 ? lse_p : plse_p) + orow * kHeads;
     auto store_half = [&](int half) {
         // wave w stores heads 32*half + 4w .. 32*half + 4w + 3; lane l holds dims
         // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
@@ -339,11 +343,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         int bstride;                // 128, or 0 for a masked token
         unsigned sbase;             // LDS byte address of the stage
     };
+    // The cache pointer, held in scalar registers for the whole kernel (the
+    // compiler otherwise reloaded it from the arguments after every step's
+    // barrier, and the wait for that load also waited for the LDS reads).
+    uint64_t kv_p = (uint64_t)(uintptr_t)a.kv;
+    asm volatile("" : "+s"(kv_p));
+    const uint8_t* const kvb = (const uint8_t*)(uintptr_t)kv_p;
     // start of the row of a physical token (v4: rows and scale records are
     // separate areas of a block)
     auto row_base = [&](int row) -> const unsigned char* {
-        if (FMT == 2) return a.kv + (int64_t)(row >> 6) * kBlockBytesV4 + (row & 63) * kRowBytesV4;
-        return a.kv + (int64_t)row * ROWB;
+        if (FMT == 2) return kvb + (int64_t)(row >> 6) * kBlockBytesV4 + (row & 63) * kRowBytesV4;
+        return kvb + (int64_t)row * ROWB;
     };
     auto prepare = [&](int tile) {
         Gather gt;
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (FMT == 1) {
             const int t2 = 8 * oct + (lane & 7);
             const int row2 = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + t2));
-            gt.src2 = row2 >= 0 ? a.kv + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
+            gt.src2 = row2 >= 0 ? kvb + (int64_t)row2 * ROWB + NBANDS * 128 : kZeroChunk;
         }
         if (FMT == 2) {
             const int th = 8 * oct + ((lane >> 2) & 7);
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             gt.src2 = rowh >= 0 ? row_base(rowh) + 4 * 128 + (((lane & 3) ^ swz4(th)) << 4) : kZeroChunk;
             const int ts = 8 * oct + ((lane >> 1) & 7);
             const int rows = *(const __attribute__((address_space(3))) int*)(rowtab + 4 * (tile * kTile + ts));
-            gt.src3 = rows >= 0 ? a.kv + (int64_t)(rows >> 6) * kBlockBytesV4 + kBlock * kRowBytesV4 +
+            gt.src3 = rows >= 0 ? kvb + (int64_t)(rows >> 6) * kBlockBytesV4 + kBlock * kRowBytesV4 +
                                       (rows & 63) * kScaleRecBytesV4 + 4 * (lane & 1)
                                 : kZeroChunk;
         }
@@ -691,10 +701,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (g == 0) {
             *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
             const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-            if (a.num_splits == 1)
-                a.lse[(int64_t)r * kHeads + head] = lse_v;
-            else
-                a.part_lse[((int64_t)sp * a.rows + r) * kHeads + head] = lse_v;
+            lbase[head] = lse_v;
         }
         __syncthreads();  // D
 #pragma unroll
