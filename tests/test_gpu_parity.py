@@ -274,10 +274,13 @@ def test_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("S", [1, 5, 70])
-def test_combine_kernel_alone(S):
+# (S, rows): up to 512 (row, head) pairs the combine runs four waves per pair, beyond that one;
+# with up to 64 parts one lse read per lane serves all weights, past 64 the parts are looped over;
+# a wave's parts go in batches of 16, 8, 4 and 1
+@pytest.mark.parametrize("S,rows", [(1, 3), (5, 3), (70, 3), (64, 3), (40, 9), (17, 9)])
+def test_combine_kernel_alone(S, rows):
     rng = np.random.default_rng(70 + S)
-    rows, H, dv = 3, 64, 512
+    H, dv = 64, 512
     po = rng.standard_normal((S, rows, H, dv)).astype(np.float32)
     pl = (rng.standard_normal((S, rows, H)) * 3).astype(np.float32)
     if S > 1:
