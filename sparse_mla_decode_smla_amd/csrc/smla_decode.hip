@@ -300,12 +300,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto store_half = [&](int half) {
         // wave w stores heads 32*half + 4w .. 32*half + 4w + 3; lane l holds dims
         // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
+        // all eight LDS reads first, then the conversions and stores (read,
+        // wait, store per head cost a round trip to LDS per head)
+        f32x4 xs[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hl = 4 * wave + j;
+            xs[j][0] = lds_load<f32x4>(lds + hl * kRowPitch + 16 * lane);
+            xs[j][1] = lds_load<f32x4>(lds + hl * kRowPitch + 1024 + 16 * lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int hl = 4 * wave + j;
             const int h = 32 * half + hl;
-            const f32x4 x0 = lds_load<f32x4>(lds + hl * kRowPitch + 16 * lane);
-            const f32x4 x1 = lds_load<f32x4>(lds + hl * kRowPitch + 1024 + 16 * lane);
+            const f32x4 x0 = xs[j][0];
+            const f32x4 x1 = xs[j][1];
             bf16x4 v0, v1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -887,12 +897,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();  // D
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            // both heads' denominators are read before any staging write (a wait
+            // for the second read would otherwise also wait for the first
+            // head block's writes)
+            float lt[2];
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) lt[hl] = lds_load<float>(aux + AUX_DENOM + 4 * (16 * (2 * half + hl) + i16));
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl) {
                 const int hb = 2 * half + hl;
                 const int h = 16 * hb + i16;
-                const float lt = lds_load<float>(aux + AUX_DENOM + 4 * h);
-                const float inv = lt == 0.f ? 0.f : 1.f / lt;
+                const float inv = lt[hl] == 0.f ? 0.f : 1.f / lt[hl];
                 lds_u8* row = lds + (h - 32 * half) * kRowPitch + 4 * (128 * p + 4 * g);
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
