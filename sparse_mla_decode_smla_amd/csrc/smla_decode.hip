@@ -275,18 +275,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
 
-    // ---- output staging: the normalised output goes through the (then idle)
-    // stage ring, so that every head's row is written to HBM with contiguous
-    // 1 KB stores.  Rows are padded by 16 bytes: the staging writes of a
-    // 16-lane group (16 heads, same dims) then fall on distinct banks.  bf16
-    // rows: the PV waves stage all 64 heads, then every wave stores 8.  The
-    // smaller rings of the fp8 layouts take 32 heads at a time: the PV waves
-    // fill a half, then every wave stores 4 of its heads.
-    constexpr int kRowPitch = 4 * kDv + 16;
-    static_assert(32 * kRowPitch <= NST * STAGE, "staging area exceeds the stage ring");
-    // bf16 rows: the ring holds all 64 heads' rows at once, so the output is
-    // staged in one round (one barrier instead of three)
-    constexpr bool ONE_ROUND = 64 * kRowPitch <= NST * STAGE;
+    // ---- output staging: the normalised output, rounded to bf16, goes through
+    // the (then idle) stage ring, so that every head's row is written to HBM
+    // with contiguous 1 KB stores.  Rows are padded by 16 bytes: the staging
+    // writes of a 16-lane group (16 heads, same dims) then fall on distinct
+    // banks.  All 64 rows fit every layout's ring: the PV waves stage every
+    // head, and after one barrier each wave stores 8 heads.
+    constexpr int kRowPitch = 2 * kDv + 16;
+    static_assert(64 * kRowPitch <= NST * STAGE, "staging area exceeds the stage ring");
     // Output rows of this workgroup: out[r] (one part) or part_out[sp][r].
     // Both pointers are taken into scalar registers before the choice.  Left
     // to itself, the compiler chose between the two argument fields' addresses
@@ -301,62 +297,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t orow = a.num_splits == 1 ? (int64_t)r : (int64_t)sp * a.rows + r;
     g_u16* const obase = (g_u16*)(uintptr_t)(a.num_splits == 1 ? out_p : part_p) + orow * kHeads * kDv;
     g_f32* const lbase = (g_f32*)(uintptr_t)(a.num_splits == 1 ? lse_p : plse_p) + orow * kHeads;
-    auto store_half = [&](int half) {
-        // wave w stores heads 32*half + 4w .. 32*half + 4w + 3; lane l holds dims
-        // [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
-        // all eight LDS reads first, then the conversions and stores (read,
-        // wait, store per head cost a round trip to LDS per head)
-        f32x4 xs[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int hl = 4 * wave + j;
-            xs[j][0] = lds_load<f32x4>(lds + hl * kRowPitch + 16 * lane);
-            xs[j][1] = lds_load<f32x4>(lds + hl * kRowPitch + 1024 + 16 * lane);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int hl = 4 * wave + j;
-            const int h = 32 * half + hl;
-            const f32x4 x0 = xs[j][0];
-            const f32x4 x1 = xs[j][1];
-            bf16x4 v0, v1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v0[e] = (__bf16)x0[e];
-                v1[e] = (__bf16)x1[e];
-            }
-            // (several parts: bf16 partials, rounded once more than the output;
-            // the combine adds them in fp32)
-            typedef __attribute__((address_space(1))) i32x2 g_i32x2;
-            g_u16* o = obase + h * kDv + 4 * lane;
-            *(g_i32x2*)o = __builtin_bit_cast(i32x2, v0);
-            *(g_i32x2*)(o + 256) = __builtin_bit_cast(i32x2, v1);
-        }
-    };
     auto store_all = [&]() {
-        // wave w stores heads 8w .. 8w + 7, all sixteen LDS reads first
-        f32x4 xs[8][2];
+        // wave w stores heads 8w .. 8w + 7; lane l holds dims [4l, 4l + 4) and
+        // [256 + 4l, 256 + 4l + 4); all sixteen LDS reads first
+        i32x2 xs[8][2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int h = 8 * wave + j;
-            xs[j][0] = lds_load<f32x4>(lds + h * kRowPitch + 16 * lane);
-            xs[j][1] = lds_load<f32x4>(lds + h * kRowPitch + 1024 + 16 * lane);
+            xs[j][0] = lds_load<i32x2>(lds + h * kRowPitch + 8 * lane);
+            xs[j][1] = lds_load<i32x2>(lds + h * kRowPitch + 512 + 8 * lane);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // (several parts: bf16 partials, rounded once more than the output; the
+        // combine adds them in fp32)
+        typedef __attribute__((address_space(1))) i32x2 g_i32x2;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int h = 8 * wave + j;
-            bf16x4 v0, v1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v0[e] = (__bf16)xs[j][0][e];
-                v1[e] = (__bf16)xs[j][1][e];
-            }
-            typedef __attribute__((address_space(1))) i32x2 g_i32x2;
-            g_u16* o = obase + h * kDv + 4 * lane;
-            *(g_i32x2*)o = __builtin_bit_cast(i32x2, v0);
-            *(g_i32x2*)(o + 256) = __builtin_bit_cast(i32x2, v1);
+            g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
+            *(g_i32x2*)o = xs[j][0];
+            *(g_i32x2*)(o + 256) = xs[j][1];
         }
     };
 
@@ -437,8 +396,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Every wave runs the same sequence of workgroup barriers: T1 and B0 (row
     // table ready), P0 (tile 0 in LDS), E_k at the end of each step k in
-    // [0, ntiles], D (denominators), then one for the staged output (bf16
-    // rows: all 64 heads fit the ring) or three (two halves).  In
+    // [0, ntiles], D (denominators), then one for the staged output.  In
     // step k the QK waves turn tile k into softmax weights P(k); the PV waves
     // add tile k-1 to the output with P(k-1) (from V held in registers) while
     // refilling the stage of tile k-1 with tile k + NST - 1, copy their V slice
@@ -744,17 +702,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             lbase[head] = lse_v;
         }
         __syncthreads();  // D
-        if (ONE_ROUND) {
-            __syncthreads();  // the PV waves have staged every head
-            store_all();
-        } else {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                __syncthreads();  // the PV waves have staged this half
-                store_half(half);
-                if (half == 0) __syncthreads();  // the staging rows are free again
-            }
-        }
+        __syncthreads();  // the PV waves have staged every head
+        store_all();
     } else {
         // ========= PV waves: value dims [128p, 128p + 128), all heads =========
         const int p = wave - 4;
@@ -930,47 +879,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         if (k <= ntiles) step(k, w1, v0, ga, gb);
         __syncthreads();  // D
-        if (ONE_ROUND) {
-            // every head block's denominator is read before any staging write (a
-            // wait for a later read would otherwise also wait for earlier writes)
-            float lt[4];
+        // every head block's denominator is read before any staging write (a
+        // wait for a later read would otherwise also wait for earlier writes);
+        // lane (head, g) holds dims 16 db + 4g .. + 3 of block db, rounded to
+        // bf16 here, once
+        float lt[4];
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) lt[hb] = lds_load<float>(aux + AUX_DENOM + 4 * (16 * hb + i16));
+        for (int hb = 0; hb < 4; ++hb) lt[hb] = lds_load<float>(aux + AUX_DENOM + 4 * (16 * hb + i16));
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                const int h = 16 * hb + i16;
-                const float inv = lt[hb] == 0.f ? 0.f : 1.f / lt[hb];
-                lds_u8* row = lds + h * kRowPitch + 4 * (128 * p + 4 * g);
+        for (int hb = 0; hb < 4; ++hb) {
+            const int h = 16 * hb + i16;
+            const float inv = lt[hb] == 0.f ? 0.f : 1.f / lt[hb];
+            lds_u8* row = lds + h * kRowPitch + 2 * (128 * p + 4 * g);
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    *(__attribute__((address_space(3))) f32x4*)(row + 64 * db) = oacc[db][hb] * inv;
+            for (int db = 0; db < 8; ++db) {
+                const f32x4 x = oacc[db][hb] * inv;
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (__bf16)x[e];
+                *(__attribute__((address_space(3))) i32x2*)(row + 32 * db) = __builtin_bit_cast(i32x2, v);
             }
-            __syncthreads();  // every head is staged
-            store_all();
-            return;
         }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // both heads' denominators are read before any staging write (a wait
-            // for the second read would otherwise also wait for the first
-            // head block's writes)
-            float lt[2];
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) lt[hl] = lds_load<float>(aux + AUX_DENOM + 4 * (16 * (2 * half + hl) + i16));
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                const int hb = 2 * half + hl;
-                const int h = 16 * hb + i16;
-                const float inv = lt[hl] == 0.f ? 0.f : 1.f / lt[hl];
-                lds_u8* row = lds + (h - 32 * half) * kRowPitch + 4 * (128 * p + 4 * g);
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    *(__attribute__((address_space(3))) f32x4*)(row + 64 * db) = oacc[db][hb] * inv;
-            }
-            __syncthreads();  // this half is staged
-            store_half(half);
-            if (half == 0) __syncthreads();  // the staging rows are free again
-        }
+        __syncthreads();  // every head is staged
+        store_all();
     }
 }
 
