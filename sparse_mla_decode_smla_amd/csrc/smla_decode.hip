@@ -396,7 +396,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Every wave runs the same sequence of workgroup barriers: T1 and B0 (row
     // table ready), P0 (tile 0 in LDS), E_k at the end of each step k in
-    // [0, ntiles], D (denominators), then one for the staged output.  In
+    // [0, ntiles] (the QK waves publish the denominators in the last one),
+    // then one for the staged output.  In
     // step k the QK waves turn tile k into softmax weights P(k); the PV waves
     // add tile k-1 to the output with P(k-1) (from V held in registers) while
     // refilling the stage of tile k-1 with tile k + NST - 1, copy their V slice
@@ -688,20 +689,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
             }
             if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 16 * (k & 1) + 4 * q) = raised;
+            if (k == ntiles) {
+                // ---- denominator and lse of `head`: final since step ntiles - 1,
+                // published in the last step (the PV waves still add the last
+                // tile), so the barrier that ends it makes them visible
+                float l_tot = l_run;
+                l_tot += __shfl_xor(l_tot, 16);
+                l_tot += __shfl_xor(l_tot, 32);
+                if (g == 0) {
+                    *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
+                    const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+                    lbase[head] = lse_v;
+                }
+            }
             if (LPT_QK > 0 && k + 1 < ntiles) wait_tiles<LPT_QK>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
             __syncthreads();  // E_k
         }
 
-        // ---- denominator and lse of `head`
-        float l_tot = l_run;
-        l_tot += __shfl_xor(l_tot, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        if (g == 0) {
-            *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
-            const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-            lbase[head] = lse_v;
-        }
-        __syncthreads();  // D
         __syncthreads();  // the PV waves have staged every head
         store_all();
     } else {
@@ -878,7 +882,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             step(k + 1, v0, w1, gb, ga);
         }
         if (k <= ntiles) step(k, w1, v0, ga, gb);
-        __syncthreads();  // D
+        // (the denominators were published in the last step: E_ntiles orders them)
         // every head block's denominator is read before any staging write (a
         // wait for a later read would otherwise also wait for earlier writes);
         // lane (head, g) holds dims 16 db + 4g .. + 3 of block db, rounded to
