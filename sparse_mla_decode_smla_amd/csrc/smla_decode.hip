@@ -864,16 +864,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             __syncthreads();  // E_k
         };
 
-        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
-        for (int t = 0; t < pro; ++t) {
+        // Only the first two tiles are gathered before P0, so that tile 0
+        // competes with fewer gathers of the other workgroups; the rest of the
+        // first NST - 1 follow P0, in order, before step 0's refill (the PV
+        // waves have nothing else to do at step 0 before it).
+        const int pro = min(NST - 1, ntiles);
+        const int pro0 = min(2, pro);  // tiles issued before P0
+        for (int t = 0; t < pro0; ++t) {
+            const Gather gt = prepare(t);
+#pragma unroll
+            for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
+        }
+        if (ntiles > 0) wait_tiles<LPT_PV>(pro0 - 1);  // this wave's part of tile 0 has landed
+        __syncthreads();  // P0
+        for (int t = pro0; t < pro; ++t) {
             const Gather gt = prepare(t);
 #pragma unroll
             for (int i = 0; i < LPT_PV; ++i) issue_one(gt, i);
         }
         Gather ga, gb;
         if (NST - 1 < ntiles) ga = prepare(NST - 1);
-        if (ntiles > 0) wait_tiles<LPT_PV>(pro - 1);  // this wave's part of tile 0 has landed
-        __syncthreads();  // P0
         VSlice v0, v1;
         VSlice& w1 = DBUF ? v1 : v0;
         int k = 0;
