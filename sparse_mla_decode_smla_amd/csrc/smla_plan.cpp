@@ -39,16 +39,17 @@ int query_cu_count(int* out) {
 
 // Estimated time (us) of one call with S parts per row, from a model fitted
 // to split sweeps of the two kernels on MI355X (256 CUs):
-//   - a workgroup gathers its part at about 30 GB/s per CU, and the whole
+//   - a workgroup gathers its part at about 35 GB/s per CU, and the whole
 //     launch at most at about 5 TB/s; a 32-token tile costs about 0.9 us of
 //     pipelined compute (bf16 rows), 1.7 us (fp8 rows, widened in registers)
 //     or 1.6 us (the pages' layout); every round of workgroups (one per CU)
 //     pays about 7.5 us of launch, prologue and epilogue;
 //   - with S > 1 every part writes 64 x 512 bf16 outputs (64 KiB) per row at
-//     about 5 TB/s; the combine kernel pays about 2.3 us, reads them back at
-//     about 8 TB/s, but a (row, head) pair's S rows of 1 KiB come in at no
-//     more than about 40 GB/s per workgroup, and 0.25 us per round of 16 part
-//     loads.
+//     about 5 TB/s; the combine kernel pays about 2.3 us, and a call about
+//     1 us more per 3 MB of partial results (their read-back and the wait
+//     between the two kernels, as timed on whole calls), but a (row, head)
+//     pair's S rows of 1 KiB come in at no more than about 40 GB/s per
+//     workgroup, and 0.25 us per round of 16 part loads.
 double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus) {
     const double row_bytes = smla::gathered_bytes_per_token(p.kv_format);
     const double t_tile = p.kv_format == SMLA_KV_BF16 ? 0.9 : p.kv_format == SMLA_KV_FP8_E4M3_SCALE128 ? 1.7 : 1.6;
@@ -57,14 +58,14 @@ double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus)
     const double rounds = std::ceil(wgs / cus);
     const double gathered = (double)rows * p.topk * row_bytes;       // upper bound: every entry valid
     const double per_wg = (double)tps * smla::kTile * row_bytes;
-    const double t_gather = std::max(per_wg / 30e3 * rounds, gathered / 5e6);  // bytes / (bytes per us)
+    const double t_gather = std::max(per_wg / 35e3 * rounds, gathered / 5e6);  // bytes / (bytes per us)
     const double t_compute = t_tile * tps * rounds;
     const double partial = S > 1 ? wgs * smla::kHeads * smla::kDv * 2.0 : 0.0;
     double t = 7.5 * rounds + std::max(t_gather, t_compute) + partial / 5e6;
     if (S > 1) {
         const double pairs = (double)rows * smla::kHeads;
         const double pair_rounds = std::ceil(pairs / (8.0 * cus));
-        t += 2.3 + std::max(partial / 8e6, S * 1024.0 / 40e3 * pair_rounds) + 0.25 * std::ceil(S / 16.0);
+        t += 2.3 + std::max(partial / 3e6, S * 1024.0 / 40e3 * pair_rounds) + 0.25 * std::ceil(S / 16.0);
     }
     return t;
 }

@@ -57,7 +57,7 @@ def test_status_strings():
 
 # split counts the plan's cost model chooses for the workloads on 256 CUs
 PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_paged_bf16": 32,
-                  "b16_topk2048_n65536_paged_bf16": 11, "b64_topk2048_n1k-128k_paged_bf16": 3,
+                  "b16_topk2048_n65536_paged_bf16": 8, "b64_topk2048_n1k-128k_paged_bf16": 3,
                   "b128_q2_topk2048_n65536_paged_fp8": 1, "b1_topk512_n8192_paged_v4fp8": 16,
                   "b64_topk512_n8192_paged_v4fp8": 4}
 
