@@ -321,7 +321,7 @@ def main() -> int:
         return traffic_summary(args.workload, *args.traffic_summary, command=args.traffic_command)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
     if args.copy_probe:
