@@ -78,6 +78,24 @@ def test_plan_covers_the_list(w):
     assert p.num_splits == PLANNED_SPLITS[w.name]
 
 
+# further shapes, each planned at the split count that measured fastest of the
+# two a cost-model change moved between (µs/call on MI355X, cold cache):
+# (batch, top-k, kv_format) -> S
+MEASURED_BEST_SPLITS = {(4, 2048, B.KV_BF16): 16,    # 17.3 against 18.2 at S=32
+                        (16, 512, B.KV_BF16): 4,     # 17.1 against 17.4 at S=8
+                        (32, 2048, B.KV_BF16): 5,    # 29.2 against 29.8 at S=6
+                        (64, 512, B.KV_BF16): 2,     # 22.5 against 23.1 at S=3
+                        (128, 1024, B.KV_BF16): 1,   # 41.8 against 46.7 at S=2
+                        (8, 2048, B.KV_FP8_E4M3_SCALE128): 16}  # 20.8 against 22.2 at S=22
+
+
+@pytest.mark.parametrize("shape", sorted(MEASURED_BEST_SPLITS), ids=str)
+def test_plan_picks_the_measured_best_split(shape):
+    batch, topk, fmt = shape
+    p = B.decode_plan(batch, 1, topk, 1024, fmt, num_cus=256)
+    assert p.num_splits == MEASURED_BEST_SPLITS[shape]
+
+
 def test_plan_splits_small_batches_more():
     """Fewer rows -> more parts per row (the occupancy argument), never more parts than tiles."""
     s = [B.decode_plan(b, 1, 2048, 1024, num_cus=256).num_splits for b in (1, 4, 16, 64, 256)]
