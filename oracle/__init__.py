@@ -50,6 +50,8 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_f32_array_to_f64.argtypes = [i64, P, P]
+    lib.oracle_f32_array_to_f64.restype = None
     lib.oracle_bf16_array_to_f64.argtypes = [i64, P, P]
     lib.oracle_bf16_array_to_f64.restype = None
     lib.oracle_e4m3fn_array_to_f64.argtypes = [i64, P, P]
@@ -82,6 +84,13 @@ class Oracle:
     def __init__(self, path: str):
         self.path = path
         self.lib = _bind(path)
+
+    def f32_to_f64(self, words: np.ndarray) -> np.ndarray:
+        """Little-endian binary32 bit patterns (uint32) -> float64, by the oracle's own decoder."""
+        words = np.ascontiguousarray(words, dtype='<u4')
+        out = np.empty(words.shape, dtype=np.float64)
+        self.lib.oracle_f32_array_to_f64(words.size, _ptr(words), _ptr(out))
+        return out
 
     def bf16_to_f64(self, bits: np.ndarray) -> np.ndarray:
         bits = np.ascontiguousarray(bits, dtype=np.uint16)

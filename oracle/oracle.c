@@ -112,7 +112,7 @@ double oracle_ue8m0_to_f64(uint8_t e)
 }
 
 /* IEEE binary32 stored little-endian. */
-static double f32_le_to_f64(const uint8_t *p)
+double oracle_f32_le_to_f64(const uint8_t *p)
 {
     uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
     int sign = (u >> 31) & 1;
@@ -129,6 +129,12 @@ static double f32_le_to_f64(const uint8_t *p)
 }
 
 static uint16_t load_u16_le(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* n little-endian binary32 values (4 bytes each) -> f64. */
+void oracle_f32_array_to_f64(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_le_to_f64(in + 4 * i);
+}
 
 void oracle_bf16_array_to_f64(int64_t n, const uint16_t *in, double *out)
 {
@@ -180,7 +186,7 @@ static void decode_token(int32_t kv_format, int32_t d_qk, int32_t d_v, int32_t b
         const uint8_t *row = block + (int64_t)slot * oracle_row_bytes(1, d_qk, d_v);
         const uint8_t *rope = row + d_v;
         const uint8_t *scales = row + d_v + 2 * (d_qk - d_v);
-        for (int d = 0; d < d_v; ++d) k[d] = oracle_e4m3fn_to_f64(row[d]) * f32_le_to_f64(scales + 4 * (d / 128));
+        for (int d = 0; d < d_v; ++d) k[d] = oracle_e4m3fn_to_f64(row[d]) * oracle_f32_le_to_f64(scales + 4 * (d / 128));
         for (int d = d_v; d < d_qk; ++d) k[d] = oracle_bf16_to_f64(load_u16_le(rope + 2 * (d - d_v)));
     } else {
         const uint8_t *row = block + (int64_t)slot * V4_DATA_BYTES;
@@ -203,7 +209,8 @@ typedef struct {
     double scale;
     double *out;
     double *lse;
-    int64_t next_row;
+    int32_t head_parts;   /* each row's heads are cut into this many contiguous ranges */
+    int64_t next_item;    /* work item i: row i / head_parts, head range i % head_parts */
     int error;
     pthread_mutex_t lock;
 } decode_job;
@@ -219,7 +226,10 @@ static int64_t physical_row(const decode_job *J, int b, int32_t p)
     return (int64_t)blk * J->block_size + p % J->block_size;
 }
 
-static void decode_one_row(decode_job *J, int64_t r, double *kbuf, double *score, double *qrow)
+/* Heads [h0, h1) of query row r.  The valid list is decoded once per call and
+ * shared by those heads; the arithmetic of a (row, head) pair does not depend
+ * on how the heads are grouped. */
+static void decode_one_row(decode_job *J, int64_t r, int h0, int h1, double *kbuf, double *score, double *qrow)
 {
     const int H = J->num_heads, DQK = J->d_qk, DV = J->d_v;
     const int b = (int)(r / J->q_len);
@@ -236,7 +246,7 @@ static void decode_one_row(decode_job *J, int64_t r, double *kbuf, double *score
         ++n;
     }
 
-    for (int h = 0; h < H; ++h) {
+    for (int h = h0; h < h1; ++h) {
         double *o = J->out + (r * H + h) * DV;
         const uint16_t *qh = J->q + (r * H + h) * DQK;
         if (n == 0) {
@@ -281,13 +291,17 @@ static void *decode_worker(void *arg)
         free(kbuf); free(score); free(qrow);
         return NULL;
     }
-    const int64_t rows = (int64_t)J->batch * J->q_len;
+    const int64_t items = (int64_t)J->batch * J->q_len * J->head_parts;
+    const int per = (J->num_heads + J->head_parts - 1) / J->head_parts;
     for (;;) {
         pthread_mutex_lock(&J->lock);
-        int64_t r = J->next_row++;
+        int64_t i = J->next_item++;
         pthread_mutex_unlock(&J->lock);
-        if (r >= rows) break;
-        decode_one_row(J, r, kbuf, score, qrow);
+        if (i >= items) break;
+        const int part = (int)(i % J->head_parts);
+        const int h0 = part * per;
+        const int h1 = h0 + per < J->num_heads ? h0 + per : J->num_heads;
+        if (h0 < h1) decode_one_row(J, i / J->head_parts, h0, h1, kbuf, score, qrow);
     }
     free(kbuf); free(score); free(qrow);
     return NULL;
@@ -301,8 +315,10 @@ static void *decode_worker(void *arg)
  * seq_lens:    int32 [batch] or NULL
  * out:         f64 [batch, q_len, num_heads, d_v]
  * lse:         f64 [batch, q_len, num_heads]
- * Rows are split over num_threads POSIX threads (<= 0 means 1); the
- * arithmetic of a row does not depend on the thread count.
+ * Work items (a query row and a contiguous range of its heads; a row's heads
+ * are cut into ranges only when there are fewer rows than threads) are split
+ * over num_threads POSIX threads (<= 0 means 1); the arithmetic of a (row,
+ * head) pair does not depend on the thread count.
  */
 int oracle_sparse_mla_decode(int32_t batch, int32_t q_len, int32_t num_heads, int32_t d_qk, int32_t d_v,
                              int32_t topk, int32_t block_size, int32_t max_blocks_per_seq,
@@ -327,11 +343,16 @@ int oracle_sparse_mla_decode(int32_t batch, int32_t q_len, int32_t num_heads, in
     J.kv_format = kv_format; J.num_kv_blocks = num_kv_blocks;
     J.q = q; J.kv_cache = kv_cache; J.block_table = block_table; J.indices = indices;
     J.seq_lens = seq_lens; J.scale = scale; J.out = out; J.lse = lse;
-    J.next_row = 0; J.error = ORACLE_OK;
+    J.next_item = 0; J.error = ORACLE_OK;
     pthread_mutex_init(&J.lock, NULL);
 
     int nt = num_threads <= 0 ? 1 : num_threads;
     if (nt > 256) nt = 256;
+    {
+        const int64_t rows = (int64_t)batch * q_len;
+        int64_t hp = rows >= nt ? 1 : (nt + rows - 1) / rows;
+        J.head_parts = (int32_t)(hp > num_heads ? num_heads : hp);
+    }
     if (nt == 1) {
         decode_worker(&J);
     } else {

@@ -326,6 +326,48 @@ def pin_single_token_v4(orc):
         assert_close(lse[0, s], (np_bf16(inp.q[0, s]) @ K) * inp.softmax_scale, 1e-12, "one token: lse")
 
 
+def pin_fp32_scale_table(orc):
+    """The oracle's binary32 decoder (the fp8 rows' scales) against numpy's float32 -> float64 widening
+    over every exponent field, zero / smallest / random / largest mantissas and both signs: subnormals,
+    normals, infinities and NaNs."""
+    rng = np.random.default_rng(40)
+    words = []
+    for e in range(256):
+        for m in (0, 1, int(rng.integers(2, 1 << 23)), (1 << 23) - 1):
+            for sign in (0, 1):
+                words.append((sign << 31) | (e << 23) | m)
+    words = np.array(words, dtype=np.uint32)
+    got = orc.f32_to_f64(words)
+    ref = words.view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN patterns"
+    assert np.array_equal(got[~nan], ref[~nan]), "binary32 decode differs from numpy's float32 widening"
+
+
+def pin_fp32_scale_rows(orc):
+    """fp8 rows whose four per-128 scales are a subnormal, the smallest normal, 1.0 and a large normal:
+    with one selected token per query row, out must be that token's V row exactly as decoded here
+    (numpy float32 view of the scale bytes) and lse its scaled score."""
+    inp = I.small_inputs(batch=1, q_len=4, topk=1, seq_len=256, kv_format=I.KV_FP8, seed=41)
+    w = inp.workload
+    scales = np.array([0x00000123, 0x00800000, 0x3F800000, 0x7E967699], dtype=np.uint32)
+    flat = inp.kv_cache.reshape(-1, w.row_bytes)
+    positions = [7, 64, 130, 255]
+    idx = np.full_like(inp.indices, -1)
+    for s, p in enumerate(positions):
+        phys = int(inp.block_table[0, p // w.block_size]) * w.block_size + p % w.block_size
+        words = np.roll(scales, s)                       # each scale value on each 128-group once
+        flat[phys, w.row_bytes - 16:] = words.astype("<u4").view(np.uint8)
+        idx[0, s, 0] = p
+    out, lse = orc.decode_inputs(inp, indices=idx)
+    for s, p in enumerate(positions):
+        K = token_rows(inp, 0, np.array([p]))[0]
+        assert np.array_equal(out[0, s], np.broadcast_to(K[: w.d_v], out[0, s].shape)), \
+            "one token with special scales: out must equal its V row exactly"
+        ref_l = (np_bf16(inp.q[0, s]) @ K) * inp.softmax_scale
+        assert np.allclose(lse[0, s], ref_l, rtol=1e-13, atol=0), "one token with special scales: lse"
+
+
 def pin_zero_query(orc):
     inp = I.small_inputs(batch=1, q_len=1, topk=77, seq_len=256, kv_format=I.KV_BF16, seed=11)
     q0 = np.zeros_like(inp.q)
@@ -451,6 +493,31 @@ def pin_indexer_scores_dense(orc):
     assert np.all(ab[fin] >= np.abs(sc[fin]) - 1e-9) and np.all(ab[~fin] == 0)
 
 
+def pin_indexer_abs_sums(orc):
+    """The indexer's per-score sums of |q_d * k_d| (the bound the GPU score check is scaled by) against a
+    numpy matmul of |q| and |k| over keys decoded here; with operands of one sign the sum is |score|."""
+    inp = I.small_indexer_inputs(batch=3, q_len=2, topk=40, seq_len_range=(50, 300), seed=26)
+    sc, ab = orc.indexer_scores(inp.q_idx, inp.k_cache, inp.block_table, inp.seq_lens)
+    w = inp.workload
+    bs, mb = w.block_size, inp.block_table.shape[1]
+    K = np.abs(np_bf16(inp.k_cache))
+    fin = np.isfinite(sc)
+    for b in range(w.batch):
+        n = min(int(inp.seq_lens[b]), bs * mb)
+        pos = np.arange(n)
+        blk = inp.block_table[b, pos // bs]
+        ref = np.abs(np_bf16(inp.q_idx[b])) @ K[blk, pos % bs].T          # [q_len, n]
+        assert_close(ab[b][:, :n][fin[b][:, :n]], ref[fin[b][:, :n]], 1e-13, "indexer abs sums")
+    # one sign: q >= 0 and k >= 0 give abs_sum == score; q <= 0 gives abs_sum == -score
+    qp = (inp.q_idx & 0x7FFF).astype(np.uint16)
+    kp = (inp.k_cache & 0x7FFF).astype(np.uint16)
+    sc2, ab2 = orc.indexer_scores(qp, kp, inp.block_table, inp.seq_lens)
+    f2 = np.isfinite(sc2)
+    assert np.array_equal(ab2[f2], sc2[f2]), "non-negative operands: abs sum must equal the score"
+    sc3, ab3 = orc.indexer_scores((qp | 0x8000).astype(np.uint16), kp, inp.block_table, inp.seq_lens)
+    assert np.array_equal(ab3[f2], -sc3[f2]), "non-positive query: abs sum must equal -score"
+
+
 def pin_indexer_topk_matches_sort(orc):
     for seed, k in ((21, 64), (22, 300)):                    # 300 > some sequences: -1 padding
         inp = I.small_indexer_inputs(batch=3, q_len=2, topk=k, seq_len_range=(100, 400), seed=seed)
@@ -507,8 +574,9 @@ def pin_indexer_masking_and_paging(orc):
 ALL_PINS = [
     pin_bf16_table, pin_e4m3_table, pin_ue8m0_table, pin_dense_bf16, pin_dense_fp8, pin_dense_v4,
     pin_dense_ragged_padded, pin_permutation, pin_split_combine, pin_paging, pin_paging_v4, pin_masking,
-    pin_seq_lens_mask, pin_empty_row, pin_single_token, pin_single_token_v4, pin_zero_query,
+    pin_seq_lens_mask, pin_empty_row, pin_single_token, pin_single_token_v4, pin_fp32_scale_table,
+    pin_fp32_scale_rows, pin_zero_query,
     pin_identical_rows, pin_identical_rows_v4, pin_duplicates, pin_combine_closed_forms,
-    pin_indexer_scores_dense, pin_indexer_topk_matches_sort, pin_indexer_ties_and_closed_form,
+    pin_indexer_scores_dense, pin_indexer_abs_sums, pin_indexer_topk_matches_sort, pin_indexer_ties_and_closed_form,
     pin_indexer_masking_and_paging,
 ]

@@ -45,8 +45,26 @@ MUTATIONS = [
      "v = ldexp(1.0 + m / 128.0, e - 127);",
      "v = ldexp(1.0 + m / 256.0, e - 127);"),
     ("fp8 scale group index wrong",
-     "* f32_le_to_f64(scales + 4 * (d / 128));",
-     "* f32_le_to_f64(scales + 4 * ((d % 128) / 32));"),
+     "* oracle_f32_le_to_f64(scales + 4 * (d / 128));",
+     "* oracle_f32_le_to_f64(scales + 4 * ((d % 128) / 32));"),
+    ("fp32 scale: subnormal exponent off by one",
+     "v = ldexp((double)m, -149);",
+     "v = ldexp((double)m, -150);"),
+    ("fp32 scale: infinity decoded as NaN",
+     "        v = (m == 0) ? INFINITY : NAN;\n    else if (e == 0)\n        v = ldexp((double)m, -149);",
+     "        v = NAN;\n    else if (e == 0)\n        v = ldexp((double)m, -149);"),
+    ("fp32 scale: exponent bias off by one",
+     "v = ldexp(1.0 + m / 8388608.0, e - 127);",
+     "v = ldexp(1.0 + m / 8388608.0, e - 126);"),
+    ("indexer abs_sum doubled",
+     "        a += fabs(t);",
+     "        a += 2.0 * fabs(t);"),
+    ("indexer abs_sum one too large per term",
+     "        a += fabs(t);",
+     "        a += fabs(t) + 1.0;"),
+    ("indexer abs_sum of signed terms",
+     "        a += fabs(t);",
+     "        a += t;"),
     ("rope elements shifted by one",
      "k[d] = oracle_bf16_to_f64(load_u16_le(rope + 2 * (d - d_v)));",
      "k[d] = oracle_bf16_to_f64(load_u16_le(rope + 2 * (d - d_v + 1)));"),
