@@ -32,7 +32,9 @@
  * Conventions:
  *   - Every buffer is owned by the caller.  The library allocates no device
  *     memory and keeps no mutable global state (the CU count of each device
- *     is cached).  Pointers are device pointers unless marked "host".
+ *     is cached), except the fixed scratch array of smla_decode_run_noalloc,
+ *     part of the library's device image.  Pointers are device pointers
+ *     unless marked "host".
  *   - smla_decode_run and smla_combine are asynchronous on `stream` (a
  *     hipStream_t; NULL = the null stream): no host synchronisation, no
  *     allocation, a launch geometry that depends only on the plan.
@@ -145,6 +147,28 @@ smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void
                               int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,
                               const int32_t *seq_lens, float softmax_scale, void *out, float *lse,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * smla_decode_run for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as smla_decode_run,
+ * without workspace: the split partial results go into a scratch array of
+ * SMLA_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per device, for the life of the process.  Plans whose workspace_bytes
+ * exceed SMLA_NOALLOC_SCRATCH_BYTES are rejected with
+ * SMLA_ERR_WORKSPACE_TOO_SMALL (use smla_decode_run with a workspace then).
+ * The first call on a device looks up that device's array (SMLA_ERR_DEVICE
+ * if the lookup fails).  Nothing in the array needs clearing: every call
+ * writes all the partial results it reads.  All calls on one device share
+ * its array, so calls that overlap in time on one device (other streams,
+ * other threads) race and may return wrong results; calls ordered on one
+ * stream are safe.  Allocates nothing; asynchronous on `stream`.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (16u << 20)
+smla_status_t smla_decode_run_noalloc(const smla_plan_t *plan, const void *q, const void *kv_cache,
+                                      int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,
+                                      const int32_t *seq_lens, float softmax_scale, void *out, float *lse,
+                                      void *stream);
 
 /*
  * The first half of smla_decode_run: the partial-attention kernel alone, with

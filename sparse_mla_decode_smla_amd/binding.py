@@ -70,6 +70,9 @@ def load(path: Optional[str] = None):
     lib.smla_decode_run.argtypes = [ctypes.POINTER(Plan), P, P, ctypes.c_int64, P, P, P, ctypes.c_float,
                                     P, P, P, ctypes.c_size_t, P]
     lib.smla_decode_run.restype = ctypes.c_int
+    lib.smla_decode_run_noalloc.argtypes = [ctypes.POINTER(Plan), P, P, ctypes.c_int64, P, P, P, ctypes.c_float,
+                                            P, P, P]
+    lib.smla_decode_run_noalloc.restype = ctypes.c_int
     lib.smla_decode_partial.argtypes = lib.smla_decode_run.argtypes
     lib.smla_decode_partial.restype = ctypes.c_int
     lib.smla_combine.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
@@ -132,6 +135,16 @@ def decode_run(plan: Plan, q, kv_cache, block_table, indices, seq_lens, softmax_
                                   _ptr(indices), _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse),
                                   _ptr(workspace), ws_bytes, _stream(stream)),
            "smla_decode_run")
+
+
+def decode_run_noalloc(plan: Plan, q, kv_cache, block_table, indices, seq_lens, softmax_scale: float, out, lse,
+                       stream=None) -> None:
+    """Enqueue smla_decode_run_noalloc (split partials in the library's own device scratch array)."""
+    num_blocks = kv_cache.shape[0] if kv_cache is not None else 0
+    _check(load().smla_decode_run_noalloc(ctypes.byref(plan), _ptr(q), _ptr(kv_cache), num_blocks,
+                                          _ptr(block_table), _ptr(indices), _ptr(seq_lens), float(softmax_scale),
+                                          _ptr(out), _ptr(lse), _stream(stream)),
+           "smla_decode_run_noalloc")
 
 
 def decode_partial(plan: Plan, q, kv_cache, block_table, indices, seq_lens, softmax_scale: float, out, lse,

@@ -1009,6 +1009,63 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
 }  // namespace
 }  // namespace smla
 
+// ---- allocation-free variant: the split partials live in a file-scope device
+// array instead of a caller's workspace.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): its
+// device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and that address is what the kernels receive.
+namespace smla {
+namespace {
+
+__device__ __attribute__((aligned(256))) unsigned char scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device); nullptr with *err set if the lookup fails.
+void* scratch_address(hipError_t* err) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {nullptr};
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+}  // namespace smla
+
+extern "C" smla_status_t smla_decode_run_noalloc(const smla_plan_t* plan, const void* q, const void* kv_cache,
+                                                 int64_t num_kv_blocks, const int32_t* block_table,
+                                                 const int32_t* indices, const int32_t* seq_lens, float softmax_scale,
+                                                 void* out, float* lse, void* stream) {
+    using namespace smla;
+    if (!plan) return SMLA_ERR_INVALID_ARG;
+    if (plan->workspace_bytes > (uint64_t)SMLA_NOALLOC_SCRATCH_BYTES) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (plan->workspace_bytes > 0) {
+        hipError_t e;
+        ws = scratch_address(&e);
+        if (!ws) return SMLA_ERR_DEVICE;
+    }
+    return smla_decode_run(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens, softmax_scale, out, lse,
+                           ws, ws ? (size_t)SMLA_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
 extern "C" smla_status_t smla_decode_partial(const smla_plan_t* plan, const void* q, const void* kv_cache,
                                              int64_t num_kv_blocks, const int32_t* block_table,
                                              const int32_t* indices, const int32_t* seq_lens, float softmax_scale,

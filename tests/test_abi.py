@@ -178,6 +178,19 @@ def test_run_argument_checks_need_no_gpu(entry, monkeypatch):
     assert v4.prob.kv_format == 2 and _run(v4, q=None) == 1
 
 
+def test_noalloc_argument_checks_need_no_gpu():
+    lib = B.load()
+
+    def run(plan, q=1 << 20):
+        return lib.smla_decode_run_noalloc(ctypes.byref(plan) if plan is not None else None, q, 1 << 21, 16,
+                                           1 << 22, 1 << 23, None, 0.04, 1 << 24, 1 << 25, None)
+    assert run(None) == 1
+    one = B.decode_plan(2, 1, 256, 8, num_cus=256, force_splits=1)
+    assert one.workspace_bytes == 0 and run(one, q=None) == 1          # checked like smla_decode_run
+    big = B.decode_plan(256, 1, 2048, 1024, num_cus=256, force_splits=2)
+    assert big.workspace_bytes > (16 << 20) and run(big) == 3           # beyond the scratch array
+
+
 def test_combine_argument_checks_need_no_gpu():
     lib = B.load()
     assert lib.smla_combine(1 << 20, 1 << 21, 0, 1, 64, 512, 1 << 22, 1 << 23, None) == 1
