@@ -4,15 +4,20 @@
 One step = one ``smla_decode_run`` call (partial-attention kernel, plus the
 log-sum-exp combine kernel when the plan splits the top-k list) over one
 batch of synthetic, seeded inputs already resident in HBM.  The default
-workload is batch 1, 64 heads, top-k 2048 over a 32768-token paged bf16
-latent cache (1152-byte rows).
+workload is the largest one that fits one GPU: batch 128 with 2 query tokens
+each (256 query rows), 64 heads, top-k 2048 over 65536-token paged latent
+caches whose c_kv part is fp8 e4m3 with one fp32 scale per 128 values
+(656-byte rows).
 
-Timing: W eager warm-up steps, then K steps captured in one HIP graph and
-replayed once between torch.cuda.synchronize() calls, timed with events on
-the stream the kernels run on.  The graph removes host launch gaps so the
-time is the GPU's.  Cold cache: consecutive steps cycle over R copies of the
-cache (R * gathered bytes >= 1 GiB, four times the 256 MB Infinity Cache),
-so a step's rows are not still cached from the previous visit.
+Timing: W eager warm-up steps, then K steps captured in one HIP graph.  The
+graph is replayed several times between torch.cuda.synchronize() calls, each
+replay timed with events on the stream the kernels run on, and the median
+replay is reported (the graph removes host launch gaps, so the time is the
+GPU's).  Cold cache: consecutive steps cycle over R copies of the cache
+(R * gathered bytes >= 1 GiB, four times the 256 MB Infinity Cache), and
+1 GiB of another buffer is read on the same stream before every timed
+replay, so no step finds its rows cached, whatever K is.  A hot figure (every step on the same
+cache copy, no flush) is reported separately and labelled.
 
 Output: one JSON line.  ``value`` = gathered-KV GB/s of the whole call
 (gathered bytes = valid selected tokens * row bytes).  ``roofline`` is for
@@ -45,8 +50,13 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-MLA decode µs/call + gathered-KV HBM GB/s (% peak), B=1..128, H=64"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "b1_topk2048_n32768_paged_bf16"
+DEFAULT_WORKLOAD = "b128_q2_topk2048_n65536_paged_fp8"
 ROTATION_BYTES = 1 << 30
+FLUSH_BYTES = 1 << 30        # read before every cold replay (4x the Infinity Cache)
+N_REPLAYS = 5                # timed replays of each graph; the median is reported
+WARM_SECONDS = 0.05          # untimed replays of each graph before timing it
+MFMA_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA peak of MI355X (both products run on bf16 MFMA)
+HOST_THREADS = 16            # host cores the CPU baseline may use (the box's share per GPU)
 MAX_COPY_BYTES = 48 << 30
 INDEXER_METRIC = "top-k indexer µs/call + indexer-key HBM GB/s (% peak)"
 KERNEL_SOURCES = ["sparse_mla_decode_smla_amd/csrc/smla_decode.hip",
@@ -91,6 +101,18 @@ def measured_traffic(workload: str):
     if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_counters(workload: str):
+    """MFMA / VALU activity of the partial kernel from the committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "valu_busy_frac", "mfma_flops_frac_of_busy") if k in rec}
 
 
 PARTIAL_KERNEL = "partial_kernel"
@@ -160,10 +182,85 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
     return 0
 
 
+def _counter_dispatches(csv_dir: str, name_part: str) -> dict:
+    """{dispatch id: {counter: value summed over its dimensions, '_us': duration}} for matching kernels."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {csv_dir}")
+    per = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if name_part not in r["Kernel_Name"]:
+                    continue
+                d = per.setdefault((f, r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not per:
+        raise ValueError(f"no dispatches of kernels matching {name_part!r} under {csv_dir}")
+    return per
+
+
+MI355X_XCDS = 8           # GRBM_GUI_ACTIVE is summed over the XCDs
+MI355X_SIMDS = 1024       # 256 CUs x 4 SIMDs
+MI355X_CUS = 256
+
+
+def counter_summary(workload: str, dir_a: str, dir_b: str, command: str) -> int:
+    """Activity counters of the partial kernel (two rocprofv3 --pmc passes) -> profiles/counters_<workload>.*
+
+    Fractions follow AMD's derived metrics: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x active
+    cycles), VALU busy = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / (SIMDs x active cycles), where active
+    cycles = GRBM_GUI_ACTIVE / XCDs.  Means over the profiled dispatches."""
+    kernel = PARTIAL_KERNEL
+    a = list(_counter_dispatches(dir_a, kernel).values())
+    b = list(_counter_dispatches(dir_b, kernel).values())
+
+    def mean(rows, f):
+        return sum(f(r) for r in rows) / len(rows)
+    cyc = lambda r: r["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+    rec = {
+        "workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(workload),
+        "dispatches": {"pass_a": len(a), "pass_b": len(b)},
+        "kernel_us": round(mean(a, lambda r: r["_us"]), 3),
+        "active_cycles_per_us": round(mean(a, lambda r: cyc(r) / r["_us"]), 1),
+        "mfma_busy_frac": round(mean(a, lambda r: r["SQ_VALU_MFMA_BUSY_CYCLES"] / (MI355X_SIMDS * cyc(r))), 4),
+        "valu_busy_frac": round(mean(a, lambda r: 4 * r["SQ_ACTIVE_INST_VALU"] / (MI355X_SIMDS * cyc(r))), 4),
+        "mfma_flops_per_launch": round(mean(a, lambda r: 512 * r["SQ_INSTS_VALU_MFMA_MOPS_BF16"])),
+        "mfma_flops_frac_of_busy": None,
+        "insts_per_launch": {"valu": round(mean(a, lambda r: r["SQ_INSTS_VALU"])),
+                             "mfma": round(mean(a, lambda r: r["SQ_INSTS_MFMA"])),
+                             "valu_cvt": round(mean(b, lambda r: r["SQ_INSTS_VALU_CVT"])),
+                             "lds": round(mean(b, lambda r: r["SQ_INSTS_LDS"]))},
+        "lds_busy_frac": round(mean(b, lambda r: r["SQ_LDS_IDX_ACTIVE"] / (MI355X_CUS * cyc(r))), 4),
+        "lds_bank_conflict_per_access": round(mean(b, lambda r: r["SQ_LDS_BANK_CONFLICT"] /
+                                                   max(1.0, r["SQ_LDS_IDX_ACTIVE"] - r["SQ_LDS_BANK_CONFLICT"])), 4),
+        "wave_wait_any_frac": round(mean(b, lambda r: r["SQ_WAIT_ANY"] / max(1.0, r["SQ_WAVE_CYCLES"]))
+                                    if "SQ_WAVE_CYCLES" in b[0] else
+                                    mean(b, lambda r: r["SQ_WAIT_ANY"] / max(1.0, r["SQ_ACTIVE_INST_ANY"] +
+                                                                            r["SQ_WAIT_ANY"])), 4),
+        "command": command,
+    }
+    # flops the busy MFMA cycles would deliver at the dense bf16 rate (16 cycles per 16x16x32 MFMA)
+    busy = mean(a, lambda r: r["SQ_VALU_MFMA_BUSY_CYCLES"])
+    rec["mfma_flops_frac_of_busy"] = round(rec["mfma_flops_per_launch"] / max(1.0, busy / 16 * 16384), 4)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
+    """The fp64 oracle on the host over a bounded sample of whole sequences of the workload, on all the
+    host cores it may use (it splits its work over (query row, head range) items, so one row fills them)."""
     import oracle
     w = inp.workload
-    threads = max(1, min(w.rows, os.cpu_count() or 1, 16))
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(nproc, HOST_THREADS))
     # bounded sample: whole sequences (all their query rows), enough of them for the threads
     nseq = max(1, min(w.batch, threads))
     sel = list(range(nseq))
@@ -174,19 +271,28 @@ def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
         oracle.default().sparse_mla_decode(inp.q[sel], inp.kv_cache, inp.block_table[sel], inp.indices[sel],
                                            inp.seq_lens[sel], inp.softmax_scale, d_v=w.d_v,
                                            kv_format=w.kv_format, block_size=w.block_size,
-                                           threads=min(threads, rows))
+                                           threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
     sample_bytes = inp.valid_count(inp.indices[sel], inp.seq_lens[sel]) * w.row_bytes * reps
-    return {"value": round(sample_bytes / el / 1e9, 6), "unit": "GB/s", "cores": min(threads, rows),
+    return {"value": round(sample_bytes / el / 1e9, 6), "unit": "GB/s", "cores": threads, "host_nproc": nproc,
             "kind": "oracle",
             "sample": f"{reps} x {nseq} sequence(s) ({rows} query rows, all 64 heads) of the workload, "
-                      f"{el:.1f} s fp64 on the host"}
+                      f"{el:.1f} s fp64 on {threads} host threads"}
 
 
-def _graph_timer(torch, stream, K):
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def _graph_timer(torch, stream, K, flush_buf=None):
+    """capture(fn) records fn(0..K-1) in one graph; time_graph(g, cold) replays it N_REPLAYS times, each
+    timed with events on `stream` (with cold, `flush_buf` is read on that stream first), and
+    returns (median us per step, [us per step of each replay])."""
     def capture(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
@@ -196,17 +302,60 @@ def _graph_timer(torch, stream, K):
                     fn(i)
         return g
 
-    def time_graph(g) -> float:
-        g.replay()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
+    def time_graph(g, cold: bool = True):
+        # (a written flush would leave dirty lines whose write-back lands in the timed replay)
+        # untimed replays for at least WARM_SECONDS first: the clock settles under sustained load
+        t0 = time.perf_counter()
+        n = 0
+        while n < 1 or (time.perf_counter() - t0 < WARM_SECONDS and n < 1000):
             g.replay()
-            s1.record(stream)
-        torch.cuda.synchronize()
-        return s0.elapsed_time(s1) * 1e3 / K
+            torch.cuda.synchronize()
+            n += 1
+        per = []
+        for rep in range(N_REPLAYS):
+            with torch.cuda.stream(stream):
+                if cold and flush_buf is not None:
+                    torch.sum(flush_buf)  # reads only: the caches hold clean lines of it afterwards
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                g.replay()
+                s1.record(stream)
+            torch.cuda.synchronize()
+            per.append(s0.elapsed_time(s1) * 1e3 / K)
+        return _median(per), per
     return capture, time_graph
+
+
+def stream_read_gbs(torch, dev, nbytes: int = 4 << 30, grid: int = 8192) -> tuple[float, str]:
+    """Measured read bandwidth of a plain streaming kernel (libsmla_probe.so: one pass of 16-byte
+    non-temporal loads over nbytes), the best of five timed calls: a second denominator next to the
+    8 TB/s peak."""
+    import ctypes
+    from sparse_mla_decode_smla_amd import build as Bd
+    lib = ctypes.CDLL(Bd.PROBE_PATH)
+    lib.smla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    lib.smla_probe_stream_read.restype = ctypes.c_int
+    x = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.smla_probe_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+        if rc != 0:
+            raise RuntimeError(f"stream-read probe failed: {rc}")
+    launch()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del x, sink
+    return nbytes / best / 1e9, f"stream-read probe over {nbytes >> 20} MiB ({grid} x 256 lanes), best of 5"
 
 
 def bench_indexer(args) -> int:
@@ -245,16 +394,17 @@ def bench_indexer(args) -> int:
     ref_idx = idx.clone()
     K = args.steps
     stream = torch.cuda.Stream(device=dev)
-    capture, time_graph = _graph_timer(torch, stream, K)
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    capture, time_graph = _graph_timer(torch, stream, K, flush_buf)
     g = capture(step)
     g.replay()
     torch.cuda.synchronize()
     if not torch.equal(idx, ref_idx):
         log("[bench] graph replay result differs from the eager result")
         return 1
-    call_us = time_graph(g)
+    call_us, _ = time_graph(g)
     del g
-    score_us = time_graph(capture(step_scores))
+    score_us, _ = time_graph(capture(step_scores))
     gbs = key_bytes / (call_us * 1e-6) / 1e9
     kernel_gbs = key_bytes / (score_us * 1e-6) / 1e9
 
@@ -288,7 +438,8 @@ def bench_indexer(args) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "topk": w.topk, "d_idx": w.d_idx,
                    "seq_len": w.seq_len if w.seq_len else list(w.seq_len_range), "key_bytes": key_bytes,
-                   "cache": f"cold: {R} rotating key-cache copies"},
+                   "cache": f"cold: steps cycle over {R} key-cache copies ({min(K, R)} per replay), "
+                            f"{FLUSH_BYTES >> 20} MiB read before each timed replay"},
         "us_per_call": round(call_us, 3),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kernels_us": {"score": round(score_us, 3), "select (call minus score)": round(call_us - score_us, 3)},
@@ -315,10 +466,14 @@ def main() -> int:
                                                             "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc csv output directories")
     ap.add_argument("--traffic-command", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PASS_A_DIR", "PASS_B_DIR"),
+                    help="write profiles/counters_<workload>.json from the two rocprofv3 --pmc activity passes")
     args = ap.parse_args()
 
     if args.traffic_summary:
         return traffic_summary(args.workload, *args.traffic_summary, command=args.traffic_command)
+    if args.counter_summary:
+        return counter_summary(args.workload, *args.counter_summary, command=args.traffic_command)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -379,27 +534,8 @@ def main() -> int:
 
     K = args.steps
     stream = torch.cuda.Stream(device=dev)
-
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(K):
-                    fn(i)
-        return g
-
-    def time_graph(g) -> float:
-        """us per step of one replay of K captured steps, timed on the capture stream."""
-        g.replay()  # warm replay
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            g.replay()
-            s1.record(stream)
-        torch.cuda.synchronize()
-        return s0.elapsed_time(s1) * 1e3 / K
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    capture, time_graph = _graph_timer(torch, stream, K, flush_buf)
 
     graph = capture(step)
     graph.replay()
@@ -407,21 +543,30 @@ def main() -> int:
     if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
         log("[bench] graph replay result differs from the eager result")
         return 1
-    call_us = time_graph(graph)
+    call_us, call_reps = time_graph(graph)
     del graph
 
     # the partial-attention kernel alone (the dominant kernel), then the combine alone
-    partial_us = time_graph(capture(step_partial))
+    partial_us, partial_reps = time_graph(capture(step_partial))
     combine_us = 0.0
     if plan.num_splits > 1:
         part_out, part_lse = B.workspace_parts(plan, ws)
         out2 = torch.empty_like(out).view(plan.rows, w.num_heads, w.d_v)
         lse2 = torch.empty_like(lse).view(plan.rows, w.num_heads)
-        combine_us = time_graph(capture(lambda i: B.combine(part_out, part_lse, out2, lse2)))
+        combine_us, _ = time_graph(capture(lambda i: B.combine(part_out, part_lse, out2, lse2)))
+    # hot: every step on the same cache copy, no flush (the rows stay in the caches)
+    hot_call_us, _ = time_graph(capture(lambda i: B.decode_run(plan, q, kv, bt, idx, sl, scale, out, lse, ws)),
+                                cold=False)
+    hot_partial_us, _ = time_graph(capture(lambda i: B.decode_partial(plan, q, kv, bt, idx, sl, scale, out, lse,
+                                                                       ws)), cold=False)
+    del copies
+    read_gbs, read_how = stream_read_gbs(torch, dev)
 
     gbs = gathered / (call_us * 1e-6) / 1e9
     kernel_gbs = gathered / (partial_us * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
+    flops = inp.valid_count() * 2 * w.num_heads * (w.d_qk + w.d_v)   # QK^T + PV per valid (row, token)
+    kernel_tflops = flops / (partial_us * 1e-6) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -430,6 +575,7 @@ def main() -> int:
 
     fmt_name = {I.KV_BF16: "bf16", I.KV_FP8: "fp8e4m3+bf16",
                 I.KV_FP8_NOPE_UE8M0: "fp8e4m3(ue8m0/64)+bf16 rope, 584 B/token pages"}[w.kv_format]
+    touched = min(K, R)
     line = {
         "metric": METRIC,
         "value": round(gbs, 3),
@@ -447,13 +593,23 @@ def main() -> int:
                    "topk": w.topk, "seq_len": w.seq_len if w.seq_len else list(w.seq_len_range),
                    "kv_format": fmt_name, "row_bytes": w.row_bytes, "gathered_bytes": gathered,
                    "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
-                   "workgroups": plan.num_workgroups, "cache": f"cold: {R} rotating cache copies"},
+                   "workgroups": plan.num_workgroups,
+                   "cache": f"cold: steps cycle over {R} cache copies ({touched} per replay), "
+                            f"{FLUSH_BYTES >> 20} MiB read before each timed replay"},
         "us_per_call": round(call_us, 3),
+        "us_per_call_replays": [round(x, 3) for x in call_reps],
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_call_eager": round(eager_us, 3),
         "kernels_us": {"partial": round(partial_us, 3), "combine": round(combine_us, 3)},
+        "hot": {"us_per_call": round(hot_call_us, 3), "partial_us": round(hot_partial_us, 3),
+                "note": "every step on the same cache copy, no flush: rows served from the caches"},
+        "stream_read": {"gbs": round(read_gbs, 1), "how": read_how,
+                        "partial_frac": round(kernel_gbs / read_gbs, 4)},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "mfma": {"achieved": round(kernel_tflops, 3), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(kernel_tflops / MFMA_PEAK_TFLOPS, 4),
+                              "counters": measured_counters(w.name)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

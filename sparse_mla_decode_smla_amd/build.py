@@ -27,8 +27,18 @@ def hipcc() -> str:
     return path
 
 
+PROBE_PATH = os.path.join(HERE, "libsmla_probe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "probe_stream.hip")]
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
+    """Build libsmla.so (the decode library) and libsmla_probe.so (the benchmark's stream-read probe)."""
+    _build_one(PROBE_SOURCES, PROBE_PATH, verbose)
+    return _build_one(SOURCES, LIB_PATH, verbose)
+
+
+def _build_one(sources, lib_path: str, verbose: bool) -> str:
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms stay disabled in the GPU code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,7 +48,7 @@ def build(verbose: bool = False) -> str:
            "-Wall", "-Wno-unused-command-line-argument"]
     for inc in INCLUDE:
         cmd += ["-I", inc]
-    cmd += ["-o", tmp, *SOURCES]
+    cmd += ["-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,8 +58,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
