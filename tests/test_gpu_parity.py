@@ -309,7 +309,9 @@ def test_combine_kernel_alone(S, rows):
 
 @pytest.mark.parametrize("splits", [1, 3])
 def test_partial_then_combine_equals_run(splits):
-    """smla_decode_partial + smla_combine is smla_decode_run, bit for bit."""
+    """smla_decode_partial + smla_combine is smla_decode_run (whose last-arriving workgroup merges the
+    parts with the combine kernel's arithmetic; the combine kernel splits a pair's parts over four waves
+    for small batches, so the sums may round differently)."""
     inp = I.small_inputs(batch=2, q_len=1, topk=300, seq_len=900, kv_format=I.KV_BF16, seed=81)
     w = inp.workload
     q, kv, bt, idx, sl = B().to_device(inp)
@@ -327,7 +329,9 @@ def test_partial_then_combine_equals_run(splits):
         B().combine(po, pl, out_b.view(plan.rows, w.num_heads, w.d_v), lse_b.view(plan.rows, w.num_heads))
     torch.cuda.synchronize()
     assert plan.num_splits == splits
-    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    oa, ob = out_a.float(), out_b.float()
+    assert float((oa - ob).abs().max()) <= 2 ** -7 * float(ob.abs().max())
+    assert float((lse_a - lse_b).abs().max()) <= 1e-5
 
 
 def test_runs_on_a_side_stream():
@@ -393,31 +397,20 @@ def workload_cache():
     return {}
 
 
-def _sample_rows(w, rng):
-    if w.rows <= 2:
-        return list(range(w.rows))
-    rows = sorted(set([0, w.rows - 1] + rng.choice(w.rows, size=min(4, w.rows), replace=False).tolist()))
-    return rows
-
-
 @pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
-def test_workload_parity_sampled_rows(w):
+def test_workload_parity_all_rows(w):
+    """Every query row of each full-size workload, in the launch configuration the benchmark times (the
+    automatic plan), against the oracle over all its sequences (16 host threads)."""
     note(f"workload {w.name}: generating")
     inp = I.make_inputs(w, seed=0)
     plan = B().decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, d_qk=w.d_qk)
     note(f"workload {w.name}: plan splits={plan.num_splits} tps={plan.tokens_per_split} wgs={plan.num_workgroups}")
-    out, lse = run_gpu(inp)   # automatic plan = the launch configuration the benchmark times
-    rng = np.random.default_rng(1)
-    rows = _sample_rows(w, rng)
-    if w.name.startswith("b64"):
-        short = [int(b) for b in np.nonzero(inp.seq_lens < w.topk)[0]]
-        rows = sorted(set(rows + short[:1]))
-    bsel = sorted(set(r // w.q_len for r in rows))
-    note(f"workload {w.name}: oracle on sequences {bsel}")
+    out, lse = run_gpu(inp)
+    note(f"workload {w.name}: oracle on all {w.rows} query rows")
     ref_o, ref_l = oracle.default().sparse_mla_decode(
-        inp.q[bsel], inp.kv_cache, inp.block_table[bsel], inp.indices[bsel], inp.seq_lens[bsel],
-        inp.softmax_scale, d_v=w.d_v, kv_format=w.kv_format, block_size=w.block_size, threads=16)
-    check(out[bsel], lse[bsel], ref_o, ref_l, f"{w.name} sequences {bsel}")
+        inp.q, inp.kv_cache, inp.block_table, inp.indices, inp.seq_lens, inp.softmax_scale, d_v=w.d_v,
+        kv_format=w.kv_format, block_size=w.block_size, threads=16)
+    check(out, lse, ref_o, ref_l, f"{w.name} all {w.rows} rows")
 
 
 def test_graph_capture_replays_v4():
