@@ -111,9 +111,7 @@ typedef struct {
     int32_t heads_per_group;     /* heads served by one workgroup */
     int32_t num_workgroups;      /* workgroups of the partial-attention kernel */
     uint64_t workspace_bytes;    /* bytes of device workspace smla_decode_run needs (0 if S = 1):
-                                    S * rows * H * (2 * d_v + 4) + 4 * rows; zero it once at
-                                    allocation (the per-row arrival counts at its end start at 0
-                                    and smla_decode_run leaves them at 0) */
+                                    S * rows * H * (2 * d_v + 4) */
 } smla_plan_t;
 
 /*
@@ -143,9 +141,7 @@ smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out
  * p >= block_size * max_blocks_per_seq, p >= seq_lens[b] (if given), or its
  * block-table entry lies outside [0, num_kv_blocks).  A row with no valid
  * entry gets out = 0 and lse = -inf.  Repeated entries count once each.
- * With several parts, the workgroup that finishes the last part of a row
- * merges the row's parts (one kernel).
- * Returns SMLA_OK after enqueueing the kernel on `stream`.
+ * Returns SMLA_OK after enqueueing the kernels on `stream`.
  */
 smla_status_t smla_decode_run(const smla_plan_t *plan, const void *q, const void *kv_cache,
                               int64_t num_kv_blocks, const int32_t *block_table, const int32_t *indices,

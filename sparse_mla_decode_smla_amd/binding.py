@@ -182,7 +182,7 @@ def alloc_workspace(plan: Plan, device):
     n = int(plan.workspace_bytes)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)   # (the per-row arrival counts start at zero)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def to_device(inp, device="cuda", indices=None):

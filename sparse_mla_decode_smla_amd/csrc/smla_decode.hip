@@ -74,8 +74,6 @@ struct PartialArgs {
     float* lse;
     uint16_t* part_out;  // bf16 partial outputs [S, rows, H, d_v]
     float* part_lse;
-    int32_t* arrivals;   // per row: parts finished (the last to arrive merges the row)
-    int32_t fuse;        // merge the parts in the last-arriving workgroup of each row
     int64_t num_kv_blocks;
     int32_t rows, q_len, topk, max_blocks, tokens_per_split, num_splits;
     float scale_log2;
@@ -155,89 +153,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_scaled_to_bf16(unsigned lo, unsigned hi
 __device__ __forceinline__ float ue8m0_scale(i32x2 rec, int sel) {
     const unsigned w = (unsigned)rec[sel >> 2];
     return __builtin_bit_cast(float, ((w >> (8 * (sel & 3))) & 0xffu) << 23);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-// Adds parts s_first .. s_first + NB - 1 of a (row, head) pair (weights in
-// lanes w_lane .. of `w`) to the accumulators, all NB loads issued first.
-template <int NB>
-__device__ __forceinline__ void merge_parts(const uint16_t* base, int64_t part_stride, int s_first, int w_lane,
-                                            float w, f32x4& acc0, f32x4& acc1) {
-    bf16x8 v[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) v[j] = *(const bf16x8*)(base + (int64_t)(s_first + j) * part_stride);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), w_lane + j));
-        const bool use = wj != 0.f;
-        f32x4 x0, x1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x0[e] = use ? (float)v[j][e] : 0.f;
-            x1[e] = use ? (float)v[j][4 + e] : 0.f;
-        }
-        acc0 += wj * x0;
-        acc1 += wj * x1;
-    }
-}
-
-// Log-sum-exp merge of the S parts of query row r, done by the workgroup
-// that finished the row's last part: wave w merges heads 8w .. 8w + 7, lane
-// l owning value dims 8l .. 8l + 7 (the same arithmetic as the combine
-// kernel).
-__device__ void merge_row(const uint16_t* part_out, const float* part_lse, int S, int64_t pairs, int r, int wave,
-                          int lane, uint16_t* out, float* lse) {
-    for (int j = 0; j < 8; ++j) {
-        const int64_t pair = (int64_t)r * kHeads + 8 * wave + j;
-        const uint16_t* base = part_out + pair * kDv + 8 * lane;
-        const int64_t stride = pairs * kDv;
-        f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-        float M = -INFINITY;
-        for (int s = lane; s < S; s += 64) M = fmaxf(M, part_lse[(int64_t)s * pairs + pair]);
-        M = wave_max(M);
-        float total = -INFINITY;
-        if (M != -INFINITY) {
-            float z = 0.f;
-            for (int s = lane; s < S; s += 64) {
-                const float l = part_lse[(int64_t)s * pairs + pair];
-                z += l == -INFINITY ? 0.f : expf(l - M);
-            }
-            total = M + logf(wave_sum(z));
-            for (int s0 = 0; s0 < S; s0 += 64) {
-                float wt = 0.f;
-                if (s0 + lane < S) {
-                    const float l = part_lse[(int64_t)(s0 + lane) * pairs + pair];
-                    wt = l == -INFINITY ? 0.f : expf(l - total);
-                }
-                const int n = min(64, S - s0);
-                int j0 = 0;
-                for (; j0 + 16 <= n; j0 += 16) merge_parts<16>(base, stride, s0 + j0, j0, wt, acc0, acc1);
-                if (j0 + 8 <= n) { merge_parts<8>(base, stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
-                if (j0 + 4 <= n) { merge_parts<4>(base, stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
-                for (; j0 < n; ++j0) merge_parts<1>(base, stride, s0 + j0, j0, wt, acc0, acc1);
-            }
-        }
-        bf16x8 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            o[e] = (__bf16)acc0[e];
-            o[4 + e] = (__bf16)acc1[e];
-        }
-        *(bf16x8*)(out + pair * kDv + 8 * lane) = o;
-        if (lane == 0) lse[pair] = total;
-    }
 }
 
 template <int N>
@@ -1002,21 +917,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();  // every head is staged
         store_all();
     }
-    // ---- fused combine: the workgroup that finishes the last part of row r
-    // merges the row's parts (its own stores and the others' are made visible
-    // device-wide by the fences around the arrival count)
-    if (a.fuse) {
-        __threadfence();
-        __syncthreads();
-        __attribute__((address_space(3))) int* const last = (__attribute__((address_space(3))) int*)(aux + AUX_FLAG);
-        if (tid == 0) *last = atomicAdd(a.arrivals + r, 1) == a.num_splits - 1;
-        __syncthreads();
-        if (*last) {
-            __threadfence();
-            merge_row(a.part_out, a.part_lse, a.num_splits, (int64_t)a.rows * kHeads, r, wave, lane, a.out, a.lse);
-            if (tid == 0) a.arrivals[r] = 0;  // zero again for the next call
-        }
-    }
 }
 
 template <int FMT>
@@ -1051,8 +951,7 @@ namespace {
 smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void* kv_cache, int64_t num_kv_blocks,
                               const int32_t* block_table, const int32_t* indices, const int32_t* seq_lens,
                               float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, PartialArgs* args_out, bool fuse = false,
-                              int32_t* arrivals = nullptr) {
+                              hipStream_t stream, PartialArgs* args_out) {
     if (!plan) return SMLA_ERR_INVALID_ARG;
     // The plan must be exactly what smla_decode_plan gives for its problem.
     smla_plan_t check;
@@ -1087,8 +986,6 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
     const int64_t pairs = (int64_t)plan->rows * kHeads;
     args.part_out = S > 1 ? (uint16_t*)workspace : nullptr;
     args.part_lse = S > 1 ? (float*)((uint16_t*)workspace + (size_t)S * pairs * kDv) : nullptr;
-    args.arrivals = S > 1 ? (arrivals ? arrivals : (int32_t*)(args.part_lse + (size_t)S * pairs)) : nullptr;
-    args.fuse = fuse && S > 1;
     args.num_kv_blocks = num_kv_blocks;
     args.rows = plan->rows;
     args.q_len = plan->prob.q_len;
@@ -1158,21 +1055,15 @@ extern "C" smla_status_t smla_decode_run_noalloc(const smla_plan_t* plan, const 
                                                  void* out, float* lse, void* stream) {
     using namespace smla;
     if (!plan) return SMLA_ERR_INVALID_ARG;
-    // (the arrival counts live at a fixed place, the last 4 KiB of the array, so that they stay zero
-    // from one call to the next whatever the plan)
-    constexpr uint64_t kCounts = 4096;
-    if (plan->workspace_bytes > (uint64_t)SMLA_NOALLOC_SCRATCH_BYTES - kCounts || 4 * (uint64_t)plan->rows > kCounts)
-        return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    if (plan->workspace_bytes > (uint64_t)SMLA_NOALLOC_SCRATCH_BYTES) return SMLA_ERR_WORKSPACE_TOO_SMALL;
     void* ws = nullptr;
     if (plan->workspace_bytes > 0) {
         hipError_t e;
         ws = scratch_address(&e);
         if (!ws) return SMLA_ERR_DEVICE;
     }
-    PartialArgs args;
-    return enqueue_partial(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens, softmax_scale, out, lse,
-                           ws, ws ? (size_t)SMLA_NOALLOC_SCRATCH_BYTES : 0, (hipStream_t)stream, &args, true,
-                           ws ? (int32_t*)((unsigned char*)ws + SMLA_NOALLOC_SCRATCH_BYTES - kCounts) : nullptr);
+    return smla_decode_run(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens, softmax_scale, out, lse,
+                           ws, ws ? (size_t)SMLA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 extern "C" smla_status_t smla_decode_partial(const smla_plan_t* plan, const void* q, const void* kv_cache,
@@ -1192,7 +1083,10 @@ extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q,
                                          void* stream) {
     using namespace smla;
     PartialArgs args;
-    // (several parts: the last-arriving workgroup of each row merges it)
-    return enqueue_partial(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens, softmax_scale, out, lse,
-                           workspace, workspace_bytes, (hipStream_t)stream, &args, true);
+    smla_status_t st = enqueue_partial(plan, q, kv_cache, num_kv_blocks, block_table, indices, seq_lens,
+                                       softmax_scale, out, lse, workspace, workspace_bytes, (hipStream_t)stream,
+                                       &args);
+    if (st != SMLA_OK || plan->rows == 0 || plan->num_splits == 1) return st;
+    return launch_combine(args.part_out, args.part_lse, plan->num_splits, (int64_t)plan->rows * kHeads, out, lse,
+                          (hipStream_t)stream);
 }

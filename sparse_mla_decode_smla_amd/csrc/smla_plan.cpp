@@ -135,10 +135,8 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
     plan.tile_tokens = kTile;
     plan.heads_per_group = kHeads;
     plan.num_workgroups = rows * splits;
-    // partial outputs and lses, then one arrival count per row (zero at allocation; the kernel
-    // zeroes a row's count again after merging it)
     plan.workspace_bytes =
-        splits > 1 ? (uint64_t)splits * (uint64_t)rows * kHeads * (kDv * 2 + 4) + 4 * (uint64_t)rows : 0;
+        splits > 1 ? (uint64_t)splits * (uint64_t)rows * kHeads * (kDv * 2 + 4) : 0;
     *plan_out = plan;
     return SMLA_OK;
 }
