@@ -35,12 +35,15 @@ KV_FP8 = 1
 KV_FP8_NOPE_UE8M0 = 2
 
 
-def build(force: bool = True, src: str = SOURCE, out_path: str = LIB_PATH) -> str:
-    """Compile an oracle source (IEEE arithmetic: no fast-math, no FMA contraction)."""
+def build(force: bool = True, src: str = SOURCE, out_path: str = LIB_PATH, sanitize: bool = False) -> str:
+    """Compile an oracle source (IEEE arithmetic: no fast-math, no FMA contraction).  With sanitize,
+    AddressSanitizer and UndefinedBehaviorSanitizer instrument it (the runtime must be preloaded into the
+    process that loads it)."""
     if force or not os.path.exists(out_path):
         tmp = out_path + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
         cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-               "-o", tmp, src, "-lm", "-lpthread"]
+               *(san if sanitize else []), "-o", tmp, src, "-lm", "-lpthread"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out_path)
     return out_path

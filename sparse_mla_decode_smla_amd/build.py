@@ -37,9 +37,20 @@ def build(verbose: bool = False) -> str:
     return _build_one(SOURCES, LIB_PATH, verbose)
 
 
-def _build_one(sources, lib_path: str, verbose: bool) -> str:
+# AddressSanitizer and UndefinedBehaviorSanitizer for the host pass only (each flag behind -Xarch_host);
+# the GPU code is built as usual.  The runtime must be preloaded into the process that loads the library.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_path: str, verbose: bool = False) -> str:
+    """libsmla.so with its host code (plan, argument checks, launch set-up) sanitized, at out_path."""
+    return _build_one(SOURCES, out_path, verbose, extra=HOST_SANITIZE)
+
+
+def _build_one(sources, lib_path: str, verbose: bool, extra=()) -> str:
     tmp = lib_path + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", *extra,
            # packed fp32 VALU forms stay disabled in the GPU code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA results in VGPRs: the partial kernel keeps Q in AGPRs and its

@@ -142,7 +142,12 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
 }
 
 extern "C" const char* smla_status_string(smla_status_t status) {
-    switch (status) {
+    // A caller may pass any int through the C ABI; reading the bits as an int keeps a value outside the
+    // enumeration well defined here (loading it as the enum type would not be).
+    int32_t code;
+    static_assert(sizeof(code) == sizeof(status), "status codes are 32-bit");
+    std::memcpy(&code, &status, sizeof(code));
+    switch (code) {
         case SMLA_OK: return "ok";
         case SMLA_ERR_INVALID_ARG: return "invalid argument";
         case SMLA_ERR_UNSUPPORTED: return "unsupported problem shape";
