@@ -195,8 +195,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int g = lane >> 4;    // 16-lane group
     const int i16 = lane & 15;  // lane within the group
 
-    const int r = blockIdx.x / a.num_splits;
-    const int sp = blockIdx.x - r * a.num_splits;
+    // (row, part) of this workgroup.  Consecutive workgroup ids are dispatched round-robin over the 8
+    // XCDs, each with its own L2; the ids are renumbered so that the parts of a row, contiguous items,
+    // share ids congruent mod 8 (one XCD), and the row's query block and block-table row come from HBM
+    // once per XCD rather than once per part.  (A bijection of [0, grid); it only affects locality.)
+    const int nwg = gridDim.x;
+    const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int item = xcd * (nwg >> 3) + min(xcd, nwg & 7) + within;
+    const int r = item / a.num_splits;
+    const int sp = item - r * a.num_splits;
     const int b = r / a.q_len;
     const int k0 = sp * a.tokens_per_split;
     const int nk = max(0, min(a.tokens_per_split, a.topk - k0));
