@@ -277,10 +277,22 @@ def cpu_baseline(inp, gathered_bytes: int, seconds: float) -> dict:
         if el >= seconds or reps >= 1000:
             break
     sample_bytes = inp.valid_count(inp.indices[sel], inp.seq_lens[sel]) * w.row_bytes * reps
+    # one thread: the first sequence's rows, for about a fifth of the time
+    t0 = time.perf_counter()
+    reps1 = 0
+    while True:
+        oracle.default().sparse_mla_decode(inp.q[:1], inp.kv_cache, inp.block_table[:1], inp.indices[:1],
+                                           inp.seq_lens[:1], inp.softmax_scale, d_v=w.d_v,
+                                           kv_format=w.kv_format, block_size=w.block_size, threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= seconds / 5 or reps1 >= 1000:
+            break
+    bytes1 = inp.valid_count(inp.indices[:1], inp.seq_lens[:1]) * w.row_bytes * reps1
     return {"value": round(sample_bytes / el / 1e9, 6), "unit": "GB/s", "cores": threads, "host_nproc": nproc,
-            "kind": "oracle",
+            "kind": "oracle", "value_1_thread": round(bytes1 / el1 / 1e9, 6),
             "sample": f"{reps} x {nseq} sequence(s) ({rows} query rows, all 64 heads) of the workload, "
-                      f"{el:.1f} s fp64 on {threads} host threads"}
+                      f"{el:.1f} s fp64 on {threads} host threads; one thread: {reps1} x sequence 0, {el1:.1f} s"}
 
 
 def _median(xs):

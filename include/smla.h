@@ -115,8 +115,15 @@ typedef struct {
 } smla_plan_t;
 
 /*
- * Fill *plan_out for *prob.  Host only; touches the device only when
- * prob->num_cus == 0 (to read the current device's CU count).
+ * Fill *plan_out for *prob: the split count S, the part length and the
+ * workspace size, a pure function of the problem shape and the CU count, so
+ * that a launch captured for a batch bucket stays valid ("The Moment of
+ * Truth: Analyzing a Custom MMA Kernel's Performance on Blackwell GPUs",
+ * "The Split-K Solution: Reasoning About the Fix": split count and scratch
+ * size fixed per batch bucket; "The Occupancy Problem: A Deeper Dive": one
+ * program per row leaves most of the GPU idle at small batch).  Host only;
+ * touches the device only when prob->num_cus == 0 (to read the current
+ * device's CU count).
  * Returns SMLA_ERR_INVALID_ARG for null pointers or negative sizes,
  * SMLA_ERR_UNSUPPORTED for shapes outside the supported set,
  * SMLA_ERR_DEVICE if the CU count cannot be read.
@@ -124,7 +131,12 @@ typedef struct {
 smla_status_t smla_decode_plan(const smla_problem_t *prob, smla_plan_t *plan_out);
 
 /*
- * Sparse MLA decode.  Shapes (R = batch * q_len, H = num_heads):
+ * Sparse MLA decode ("The MMA Sparse-MLA Decode Kernel: A Deep Dive into AI
+ * Inference Optimization on Blackwell GPUs", Agent Reasoning: "Kernel
+ * Structure Analysis" for the operation, "Design Decisions" 1 and 3 for the
+ * head batching and the split over the top-k list, "Edge Case Handling" for
+ * the masking; "Validation Strategy": the results are out and lse).
+ * Shapes (R = batch * q_len, H = num_heads):
  *   q            bf16  [batch, q_len, H, d_qk]
  *   kv_cache     bytes [num_kv_blocks, block bytes of kv_format]
  *   block_table  int32 [batch, max_blocks_per_seq]: physical block of each
