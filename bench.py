@@ -338,6 +338,46 @@ def _graph_timer(torch, stream, K, flush_buf=None):
     return capture, time_graph
 
 
+def gather_probe(nbytes: int = 16 << 30, ntiles: int = 64, reps: int = 3) -> int:
+    """Random 1152-byte rows gathered into LDS by LDS-DMA with four instruction patterns (libsmla_probe.so,
+    no compute), at 128 and 256 workgroups; one JSON line per (mode, workgroups) with the best of `reps`."""
+    import ctypes
+    import numpy as np
+    import torch
+    from sparse_mla_decode_smla_amd import build as Bd
+    lib = ctypes.CDLL(Bd.PROBE_PATH)
+    lib.smla_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.smla_probe_gather.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    nrows = nbytes // 1152
+    buf = torch.ones(nrows * 1152, dtype=torch.uint8, device=dev)
+    rng = np.random.default_rng(0)
+    names = {0: "8 rows x 128 B, 8 lanes per row (band-major, as the kernel)", 1: "1 row x 1024 B (row-major)",
+             2: "8 rows x 128 B, lanes by half band", 3: "8 rows x 128 B, lanes interleaved by row"}
+    for grid in (128, 256):
+        rows = torch.from_numpy(rng.integers(0, nrows, size=grid * ntiles * 32, dtype=np.int32)).to(dev)
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        for mode in range(4):
+            best = float("inf")
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rc = lib.smla_probe_gather(buf.data_ptr(), rows.data_ptr(), ntiles, mode, sink.data_ptr(), grid,
+                                           stream)
+                e1.record()
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"gather probe failed: {rc}")
+                best = min(best, e0.elapsed_time(e1) * 1e-3)
+            moved = grid * ntiles * 32 * 1152
+            print(json.dumps({"gather_probe": names[mode], "mode": mode, "workgroups": grid, "rows": grid * ntiles * 32,
+                              "us": round(best * 1e6, 1), "tb_per_s": round(moved / best / 1e12, 3),
+                              "gb_per_s_per_workgroup": round(moved / grid / best / 1e9, 2)}), flush=True)
+    return 0
+
+
 def stream_read_gbs(torch, dev, nbytes: int = 4 << 30, grid: int = 8192) -> tuple[float, str]:
     """Measured read bandwidth of a plain streaming kernel (libsmla_probe.so: one pass of 16-byte
     non-temporal loads over nbytes), the best of five timed calls: a second denominator next to the
@@ -474,6 +514,8 @@ def main() -> int:
     ap.add_argument("--force-splits", type=int, default=0, help="override the planned split count (sweeps)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain streaming kernel of known size (counter calibration)")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="run only the row-gather probe (LDS-DMA instruction patterns, no compute)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                             "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc csv output directories")
@@ -493,6 +535,8 @@ def main() -> int:
         return 2
     if args.copy_probe:
         return copy_probe()
+    if args.gather_probe:
+        return gather_probe()
 
     import numpy as np
     import torch
