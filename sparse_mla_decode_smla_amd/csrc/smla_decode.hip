@@ -76,6 +76,7 @@ struct PartialArgs {
     float* part_lse;
     int64_t num_kv_blocks;
     int32_t rows, q_len, topk, max_blocks, tokens_per_split, num_splits;
+    int32_t num_workgroups;  // the grid size (read here rather than from the dispatch packet)
     float scale_log2;
 };
 
@@ -169,7 +170,16 @@ __device__ __forceinline__ void wait_tiles(int after) {
 
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void partial_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void partial_kernel(PartialArgs a_arg) {
+    // Every argument is taken into scalar registers here, in one batch of
+    // loads with one wait: left to itself, the compiler read the argument
+    // block in pieces where each field was first used, each piece one more
+    // dependent round trip before the first memory access of the list.
+    PartialArgs a = a_arg;
+    asm volatile("" : "+s"(a.q), "+s"(a.kv), "+s"(a.block_table), "+s"(a.indices), "+s"(a.seq_lens), "+s"(a.out),
+                 "+s"(a.lse), "+s"(a.part_out), "+s"(a.part_lse), "+s"(a.num_kv_blocks), "+s"(a.rows),
+                 "+s"(a.q_len), "+s"(a.topk), "+s"(a.max_blocks), "+s"(a.tokens_per_split), "+s"(a.num_splits),
+                 "+s"(a.num_workgroups), "+s"(a.scale_log2));
     constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : FMT == 1 ? kStageBytesFp8 : kStageBytesV4;
     constexpr int NST = FMT == 0 ? kStagesBf16 : FMT == 1 ? kStagesFp8 : kStagesV4;
     constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : FMT == 1 ? kRowBytesFp8 : kRowBytesV4;
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // XCDs, each with its own L2; the ids are renumbered so that the parts of a row, contiguous items,
     // share ids congruent mod 8 (one XCD), and the row's query block and block-table row come from HBM
     // once per XCD rather than once per part.  (A bijection of [0, grid); it only affects locality.)
-    const int nwg = gridDim.x;
+    const int nwg = a.num_workgroups;
     const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
     const int item = xcd * (nwg >> 3) + min(xcd, nwg & 7) + within;
     const int r = item / a.num_splits;
@@ -1001,6 +1011,7 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
     args.tokens_per_split = plan->tokens_per_split;
     args.num_splits = S;
     args.scale_log2 = softmax_scale * kLog2e;
+    args.num_workgroups = plan->num_workgroups;
 
     const size_t lds = partial_lds_bytes(plan->prob.kv_format, plan->tokens_per_split);
     (void)hipGetLastError();  // clear an earlier, unrelated error
