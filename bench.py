@@ -512,6 +512,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=0, help="override the planned split count (sweeps)")
+    ap.add_argument("--cache-policy", default="auto", choices=["auto", "cached", "stream-rows", "stream-out",
+                                                                "stream-both"],
+                    help="cache hints of the row gathers and result stores (auto: the plan's choice)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain streaming kernel of known size (counter calibration)")
     ap.add_argument("--gather-probe", action="store_true",
@@ -554,7 +557,7 @@ def main() -> int:
     gathered = inp.valid_count() * w.row_bytes
     q, kv, bt, idx, sl = B.to_device(inp, device=dev)
     plan = B.decode_plan(w.batch, w.q_len, w.topk, inp.block_table.shape[1], w.kv_format, d_qk=w.d_qk,
-                         force_splits=args.force_splits)
+                         force_splits=args.force_splits, cache_policy=B.CACHE_POLICY_NAMES[args.cache_policy])
     out = torch.empty((w.batch, w.q_len, w.num_heads, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.q_len, w.num_heads), dtype=torch.float32, device=dev)
     ws = B.alloc_workspace(plan, dev)
@@ -650,6 +653,7 @@ def main() -> int:
                    "kv_format": fmt_name, "row_bytes": w.row_bytes, "gathered_bytes": gathered,
                    "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
                    "workgroups": plan.num_workgroups,
+                   "cache_policy": {v: k for k, v in B.CACHE_POLICY_NAMES.items()}[plan.cache_policy],
                    "cache": f"cold: steps cycle over {R} cache copies ({touched} per replay), "
                             f"{FLUSH_BYTES >> 20} MiB read before each timed replay"},
         "us_per_call": round(call_us, 3),

@@ -82,6 +82,22 @@ typedef enum {
     SMLA_KV_FP8_NOPE_UE8M0 = 2
 } smla_kv_format_t;
 
+/* Cache policy of the partial-attention kernel's memory traffic.  "Streaming"
+ * marks the accesses non-temporal (the nt bit of gfx950 loads and stores: no
+ * reuse expected, so the caches keep other data).  Rows: the gathered latent
+ * rows; out: the per-part results (or the output with one part).  The
+ * arithmetic, and so every result, is the same under every policy.
+ * SMLA_CACHE_AUTO lets the plan choose from the problem shape: streaming rows
+ * when the call may gather at least 64 MiB, streaming outputs when it writes
+ * at least 4 MiB (thresholds set by measurement on MI355X). */
+typedef enum {
+    SMLA_CACHE_AUTO = 0,
+    SMLA_CACHE_CACHED = 1,          /* rows and outputs through the caches as ordinary accesses */
+    SMLA_CACHE_STREAM_ROWS = 2,     /* streaming row gathers, cached outputs */
+    SMLA_CACHE_STREAM_OUT = 3,      /* cached row gathers, streaming outputs */
+    SMLA_CACHE_STREAM_BOTH = 4      /* streaming row gathers and outputs */
+} smla_cache_policy_t;
+
 /* Problem description (host).  Supported: num_heads = 64, d_v = 512,
  * block_size = 64, d_qk = 576 (kv_format 0, 1) or 512 (kv_format 2); any
  * batch >= 0, q_len >= 1, topk >= 0. */
@@ -97,7 +113,7 @@ typedef struct {
     int32_t kv_format;           /* smla_kv_format_t */
     int32_t num_cus;             /* compute units to fill; 0 = query the current device */
     int32_t force_splits;        /* 0 = choose automatically; > 0 = use this split count (clamped to the tile count) */
-    int32_t reserved;            /* must be 0 */
+    int32_t cache_policy;        /* smla_cache_policy_t: 0 = choose automatically */
 } smla_problem_t;
 
 /* Plan: a pure function of the problem (identical problems give identical
@@ -112,6 +128,8 @@ typedef struct {
     int32_t num_workgroups;      /* workgroups of the partial-attention kernel */
     uint64_t workspace_bytes;    /* bytes of device workspace smla_decode_run needs (0 if S = 1):
                                     S * rows * H * (2 * d_v + 4) */
+    int32_t cache_policy;        /* the policy in force (never SMLA_CACHE_AUTO) */
+    int32_t reserved;            /* 0 */
 } smla_plan_t;
 
 /*

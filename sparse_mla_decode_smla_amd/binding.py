@@ -20,6 +20,15 @@ KV_BF16 = 0
 KV_FP8_E4M3_SCALE128 = 1
 KV_FP8_NOPE_UE8M0 = 2
 
+# smla_cache_policy_t
+CACHE_AUTO = 0
+CACHE_CACHED = 1
+CACHE_STREAM_ROWS = 2
+CACHE_STREAM_OUT = 3
+CACHE_STREAM_BOTH = 4
+CACHE_POLICY_NAMES = {"auto": CACHE_AUTO, "cached": CACHE_CACHED, "stream-rows": CACHE_STREAM_ROWS,
+                      "stream-out": CACHE_STREAM_OUT, "stream-both": CACHE_STREAM_BOTH}
+
 STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED",
           3: "SMLA_ERR_WORKSPACE_TOO_SMALL", 4: "SMLA_ERR_LAUNCH", 5: "SMLA_ERR_DEVICE"}
 
@@ -35,14 +44,15 @@ class Problem(ctypes.Structure):
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("kv_format", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("force_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("force_splits", ctypes.c_int32), ("cache_policy", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
     _fields_ = [("prob", Problem), ("rows", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("tokens_per_split", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
                 ("heads_per_group", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("cache_policy", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "prob"}
@@ -103,9 +113,9 @@ def _check(status: int, where: str):
 
 def decode_plan(batch: int, q_len: int, topk: int, max_blocks_per_seq: int, kv_format: int = KV_BF16, *,
                 num_heads: int = 64, d_qk: int = 576, d_v: int = 512, block_size: int = 64,
-                num_cus: int = 0, force_splits: int = 0) -> Plan:
+                num_cus: int = 0, force_splits: int = 0, cache_policy: int = CACHE_AUTO) -> Plan:
     prob = Problem(batch, q_len, num_heads, d_qk, d_v, topk, block_size, max_blocks_per_seq, kv_format,
-                   num_cus, force_splits, 0)
+                   num_cus, force_splits, cache_policy)
     plan = Plan()
     _check(load().smla_decode_plan(ctypes.byref(prob), ctypes.byref(plan)), "smla_decode_plan")
     return plan
@@ -210,13 +220,13 @@ def to_device(inp, device="cuda", indices=None):
 
 
 def sparse_mla_decode(q, kv_cache, block_table, indices, seq_lens, softmax_scale: float,
-                      kv_format: int = KV_BF16, force_splits: int = 0, stream=None):
+                      kv_format: int = KV_BF16, force_splits: int = 0, stream=None, cache_policy: int = CACHE_AUTO):
     """Plan, allocate (torch) and run; returns (out bf16 [B, q_len, H, d_v], lse fp32 [B, q_len, H])."""
     import torch
     B, q_len, H, d_qk = q.shape
     topk = indices.shape[2]
     plan = decode_plan(B, q_len, topk, block_table.shape[1], kv_format, num_heads=H, d_qk=d_qk,
-                       force_splits=force_splits)
+                       force_splits=force_splits, cache_policy=cache_policy)
     out = torch.empty((B, q_len, H, plan.prob.d_v), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, q_len, H), dtype=torch.float32, device=q.device)
     ws = alloc_workspace(plan, q.device)

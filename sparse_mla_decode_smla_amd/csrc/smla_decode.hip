@@ -77,6 +77,7 @@ struct PartialArgs {
     int64_t num_kv_blocks;
     int32_t rows, q_len, topk, max_blocks, tokens_per_split, num_splits;
     int32_t num_workgroups;  // the grid size (read here rather than from the dispatch packet)
+    int32_t stream_out;      // 1: the results are written with non-temporal stores
     float scale_log2;
 };
 
@@ -84,12 +85,19 @@ struct PartialArgs {
 // lds_base + 16*l (lds_base is the same in every lane).  Issued from inline assembly so the compiler does not
 // serialise the stage ring with conservative waits; the kernel waits on
 // vmcnt itself.  M0 is written only here (the kernel has no other M0 use).
+// NT: the load is marked non-temporal (streaming row gathers).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
+    if (NT)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory", "m0");
 }
 // 4-byte variant: lane l's 4 bytes land at lds_base + 4*l.
 __device__ __forceinline__ void lds_dma4(const void* src, unsigned lds_base) {
@@ -169,7 +177,8 @@ __device__ __forceinline__ void wait_tiles(int after) {
 }
 
 
-template <int FMT>
+// NTG: the row gathers are non-temporal loads.
+template <int FMT, bool NTG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void partial_kernel(PartialArgs a_arg) {
     // Every argument is taken into scalar registers here, in one batch of
     // loads with one wait: left to itself, the compiler read the argument
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     asm volatile("" : "+s"(a.q), "+s"(a.kv), "+s"(a.block_table), "+s"(a.indices), "+s"(a.seq_lens), "+s"(a.out),
                  "+s"(a.lse), "+s"(a.part_out), "+s"(a.part_lse), "+s"(a.num_kv_blocks), "+s"(a.rows),
                  "+s"(a.q_len), "+s"(a.topk), "+s"(a.max_blocks), "+s"(a.tokens_per_split), "+s"(a.num_splits),
-                 "+s"(a.num_workgroups), "+s"(a.scale_log2));
+                 "+s"(a.num_workgroups), "+s"(a.stream_out), "+s"(a.scale_log2));
     constexpr int STAGE = FMT == 0 ? kStageBytesBf16 : FMT == 1 ? kStageBytesFp8 : kStageBytesV4;
     constexpr int NST = FMT == 0 ? kStagesBf16 : FMT == 1 ? kStagesFp8 : kStagesV4;
     constexpr int ROWB = FMT == 0 ? kRowBytesBf16 : FMT == 1 ? kRowBytesFp8 : kRowBytesV4;
@@ -328,11 +337,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // (several parts: bf16 partials, rounded once more than the output; the
         // combine adds them in fp32)
         typedef __attribute__((address_space(1))) i32x2 g_i32x2;
+        if (a.stream_out) {
+            // (non-temporal stores written out: with the builtin, the compiler merged
+            // the two branches' identical stores and dropped the hint)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
-            *(g_i32x2*)o = xs[j][0];
-            *(g_i32x2*)(o + 256) = xs[j][1];
+            for (int j = 0; j < 8; ++j) {
+                g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
+                asm volatile("global_store_dwordx2 %0, %1, off nt\n\tglobal_store_dwordx2 %0, %2, off offset:512 nt"
+                             ::"v"(o), "v"(xs[j][0]), "v"(xs[j][1])
+                             : "memory");
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
+                *(g_i32x2*)o = xs[j][0];
+                *(g_i32x2*)(o + 256) = xs[j][1];
+            }
         }
     };
 
@@ -400,11 +421,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto issue_one = [&](const Gather& gt, int i) {  // DMA i of this wave's share of a tile
         const int bd = band0 + i;
         if (bd < NBANDS)
-            lds_dma16(gt.src + bd * gt.bstride, gt.sbase + (unsigned)((bd * kTile + 8 * oct) * 128));
+            lds_dma16<NTG>(gt.src + bd * gt.bstride, gt.sbase + (unsigned)((bd * kTile + 8 * oct) * 128));
         else if (FMT == 1) {
-            if (lane < 8) lds_dma16(gt.src2, gt.sbase + (unsigned)(NBANDS * kTile * 128 + 8 * oct * 16));
+            if (lane < 8) lds_dma16<NTG>(gt.src2, gt.sbase + (unsigned)(NBANDS * kTile * 128 + 8 * oct * 16));
         } else if (bd == NBANDS) {
-            if (lane < 32) lds_dma16(gt.src2, gt.sbase + (unsigned)(HALF_OFF + 8 * oct * 64));
+            if (lane < 32) lds_dma16<NTG>(gt.src2, gt.sbase + (unsigned)(HALF_OFF + 8 * oct * 64));
         } else {
             if (lane < 16) lds_dma4(gt.src3, gt.sbase + (unsigned)(REC_OFF + 8 * oct * kScaleRecBytesV4));
         }
@@ -936,7 +957,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int FMT>
+template <int FMT, bool NTG>
 hipError_t launch_partial(const PartialArgs& args, int grid, size_t lds_bytes, hipStream_t stream) {
     static std::mutex mu;
     static bool configured[64] = {false};
@@ -946,13 +967,13 @@ hipError_t launch_partial(const PartialArgs& args, int grid, size_t lds_bytes, h
     {
         std::lock_guard<std::mutex> lock(mu);
         if (dev < 0 || dev >= 64 || !configured[dev]) {
-            e = hipFuncSetAttribute((const void*)partial_kernel<FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kLdsLimit);
+            e = hipFuncSetAttribute((const void*)partial_kernel<FMT, NTG>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
             if (e != hipSuccess) return e;
             if (dev >= 0 && dev < 64) configured[dev] = true;
         }
     }
-    hipLaunchKernelGGL(partial_kernel<FMT>, dim3(grid), dim3(kThreads), lds_bytes, stream, args);
+    hipLaunchKernelGGL((partial_kernel<FMT, NTG>), dim3(grid), dim3(kThreads), lds_bytes, stream, args);
     return hipGetLastError();
 }
 
@@ -1012,14 +1033,24 @@ smla_status_t enqueue_partial(const smla_plan_t* plan, const void* q, const void
     args.num_splits = S;
     args.scale_log2 = softmax_scale * kLog2e;
     args.num_workgroups = plan->num_workgroups;
+    const int pol = plan->cache_policy;
+    const bool ntg = pol == SMLA_CACHE_STREAM_ROWS || pol == SMLA_CACHE_STREAM_BOTH;
+    args.stream_out = pol == SMLA_CACHE_STREAM_OUT || pol == SMLA_CACHE_STREAM_BOTH ? 1 : 0;
 
     const size_t lds = partial_lds_bytes(plan->prob.kv_format, plan->tokens_per_split);
     (void)hipGetLastError();  // clear an earlier, unrelated error
     hipError_t e;
+    const int g = plan->num_workgroups;
     switch (plan->prob.kv_format) {
-        case SMLA_KV_BF16: e = launch_partial<0>(args, plan->num_workgroups, lds, stream); break;
-        case SMLA_KV_FP8_E4M3_SCALE128: e = launch_partial<1>(args, plan->num_workgroups, lds, stream); break;
-        default: e = launch_partial<2>(args, plan->num_workgroups, lds, stream); break;
+        case SMLA_KV_BF16:
+            e = ntg ? launch_partial<0, true>(args, g, lds, stream) : launch_partial<0, false>(args, g, lds, stream);
+            break;
+        case SMLA_KV_FP8_E4M3_SCALE128:
+            e = ntg ? launch_partial<1, true>(args, g, lds, stream) : launch_partial<1, false>(args, g, lds, stream);
+            break;
+        default:
+            e = ntg ? launch_partial<2, true>(args, g, lds, stream) : launch_partial<2, false>(args, g, lds, stream);
+            break;
     }
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }

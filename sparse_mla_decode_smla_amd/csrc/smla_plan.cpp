@@ -70,6 +70,25 @@ double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus)
     return t;
 }
 
+// Streaming (non-temporal) row gathers when a call may gather 64 MiB or more,
+// streaming outputs when it writes 4 MiB or more.  Measured on MI355X with
+// the benchmark's workloads (cold cache, HIP graphs): streaming rows took the
+// batch-64 top-2048 bf16 call from 41.4 to 39.1 us (with streaming outputs)
+// and the fp8 batch-128 call from 109.6 to 106.1 us, but slowed calls that
+// gather 38 MB or less (batch 16: 21.7 to 23.2 us); streaming outputs helped
+// once a call writes 8 MB or more (batch 16: 21.7 to 21.2 us) and slowed the
+// batch-1 calls, which write 1 to 2 MB (13.6 to 14.0 us).
+int choose_cache_policy(const smla_problem_t& p, int rows, int splits) {
+    const double gathered = (double)rows * p.topk * smla::gathered_bytes_per_token(p.kv_format);
+    const double written = (double)rows * splits * smla::kHeads * smla::kDv * 2.0;
+    const bool rows_stream = gathered >= 64.0 * (1 << 20);
+    const bool out_stream = written >= 4.0 * (1 << 20);
+    if (rows_stream && out_stream) return SMLA_CACHE_STREAM_BOTH;
+    if (rows_stream) return SMLA_CACHE_STREAM_ROWS;
+    if (out_stream) return SMLA_CACHE_STREAM_OUT;
+    return SMLA_CACHE_CACHED;
+}
+
 int choose_splits(const smla_problem_t& p, int rows, int tiles, int cap_tiles, int cus) {
     if (rows <= 0 || tiles <= 1) return 1;
     const int min_s = (tiles + cap_tiles - 1) / cap_tiles;  // parts small enough for the LDS row table
@@ -92,7 +111,7 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
     if (!prob || !plan_out) return SMLA_ERR_INVALID_ARG;
     const smla_problem_t& p = *prob;
     if (p.batch < 0 || p.q_len < 1 || p.topk < 0 || p.max_blocks_per_seq < 1 || p.num_cus < 0 ||
-        p.force_splits < 0 || p.reserved != 0)
+        p.force_splits < 0 || p.cache_policy < SMLA_CACHE_AUTO || p.cache_policy > SMLA_CACHE_STREAM_BOTH)
         return SMLA_ERR_INVALID_ARG;
     if (p.kv_format != SMLA_KV_BF16 && p.kv_format != SMLA_KV_FP8_E4M3_SCALE128 &&
         p.kv_format != SMLA_KV_FP8_NOPE_UE8M0)
@@ -137,6 +156,7 @@ extern "C" smla_status_t smla_decode_plan(const smla_problem_t* prob, smla_plan_
     plan.num_workgroups = rows * splits;
     plan.workspace_bytes =
         splits > 1 ? (uint64_t)splits * (uint64_t)rows * kHeads * (kDv * 2 + 4) : 0;
+    plan.cache_policy = p.cache_policy != SMLA_CACHE_AUTO ? p.cache_policy : choose_cache_policy(p, rows, splits);
     *plan_out = plan;
     return SMLA_OK;
 }

@@ -37,8 +37,9 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "smla.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu\\n", sizeof(smla_problem_t), sizeof(smla_plan_t),
-         offsetof(smla_plan_t, rows), offsetof(smla_plan_t, num_workgroups), offsetof(smla_plan_t, workspace_bytes));
+  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(smla_problem_t), sizeof(smla_plan_t),
+         offsetof(smla_plan_t, rows), offsetof(smla_plan_t, num_workgroups), offsetof(smla_plan_t, workspace_bytes),
+         offsetof(smla_problem_t, cache_policy), offsetof(smla_plan_t, cache_policy));
   return 0;
 }
 """)
@@ -46,7 +47,8 @@ int main(void) {
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(B.Problem), ctypes.sizeof(B.Plan), B.Plan.rows.offset,
-                   B.Plan.num_workgroups.offset, B.Plan.workspace_bytes.offset]
+                   B.Plan.num_workgroups.offset, B.Plan.workspace_bytes.offset, B.Problem.cache_policy.offset,
+                   B.Plan.cache_policy.offset]
 
 
 def test_status_strings():
@@ -60,6 +62,40 @@ PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_pa
                   "b16_topk2048_n65536_paged_bf16": 8, "b64_topk2048_n1k-128k_paged_bf16": 3,
                   "b128_q2_topk2048_n65536_paged_fp8": 1, "b1_topk512_n8192_paged_v4fp8": 16,
                   "b64_topk512_n8192_paged_v4fp8": 4}
+
+
+# cache policies the plan chooses automatically: streaming rows from 64 MiB of gathered rows (upper
+# bound rows * topk * row bytes), streaming outputs from 4 MiB of results written by the partial kernel
+PLANNED_POLICY = {"b1_topk512_n4096_contiguous_bf16": B.CACHE_CACHED, "b1_topk2048_n32768_paged_bf16": B.CACHE_CACHED,
+                  "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_OUT,
+                  "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_BOTH,
+                  "b128_q2_topk2048_n65536_paged_fp8": B.CACHE_STREAM_BOTH,
+                  "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_OUT}
+
+
+@pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
+def test_plan_cache_policy(w):
+    mb = (w.max_seq_len + 63) // 64
+    p = B.decode_plan(w.batch, w.q_len, w.topk, mb, w.kv_format, d_qk=w.d_qk, num_cus=256)
+    assert p.prob.cache_policy == B.CACHE_AUTO and p.cache_policy == PLANNED_POLICY[w.name]
+    for pol in (B.CACHE_CACHED, B.CACHE_STREAM_ROWS, B.CACHE_STREAM_OUT, B.CACHE_STREAM_BOTH):
+        q = B.decode_plan(w.batch, w.q_len, w.topk, mb, w.kv_format, d_qk=w.d_qk, num_cus=256, cache_policy=pol)
+        assert q.cache_policy == pol and q.num_splits == p.num_splits and q.workspace_bytes == p.workspace_bytes
+
+
+def test_plan_cache_policy_thresholds():
+    # bf16 rows (1152 bytes): 64 MiB of rows = 58254 selected tokens; one part of 64 KiB per row
+    rows = B.decode_plan(29, 1, 2048, 64, num_cus=256, force_splits=1)     # 65.3 MiB rows, 1.8 MiB out
+    assert rows.cache_policy == B.CACHE_STREAM_ROWS
+    below = B.decode_plan(28, 1, 2048, 64, num_cus=256, force_splits=1)    # 63.0 MiB rows
+    assert below.cache_policy == B.CACHE_CACHED
+    tiny = B.decode_plan(2, 1, 2048, 64, num_cus=256, force_splits=1)      # 4.7 MB rows, 128 KiB out
+    assert tiny.cache_policy == B.CACHE_CACHED
+    out = B.decode_plan(64, 1, 32, 64, num_cus=256, force_splits=1)        # 2.4 MB rows, 4 MiB out
+    assert out.cache_policy == B.CACHE_STREAM_OUT
+    for bad in (-1, 5):
+        with pytest.raises(B.SmlaError):
+            B.decode_plan(1, 1, 64, 4, num_cus=256, cache_policy=bad)
 
 
 @pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)

@@ -48,19 +48,32 @@ def check(out_gpu, lse_gpu, out_ref, lse_ref, what):
     assert lerr <= LSE_ABS, f"{what}: lse err {lerr:.3e}"
 
 
-def run_gpu(inp, indices=None, force_splits=0, with_seq_lens=True, block_table=None):
+def run_gpu(inp, indices=None, force_splits=0, with_seq_lens=True, block_table=None, cache_policy=0):
     w = inp.workload
     q, kv, bt, idx, sl = B().to_device(inp, indices=indices)
     if block_table is not None:
         bt = torch.from_numpy(block_table).cuda()
     out, lse = B().sparse_mla_decode(q, kv, bt, idx, sl if with_seq_lens else None, inp.softmax_scale,
-                                     kv_format=w.kv_format, force_splits=force_splits)
+                                     kv_format=w.kv_format, force_splits=force_splits, cache_policy=cache_policy)
     torch.cuda.synchronize()
     return out, lse
 
 
 FORMATS = [I.KV_BF16, I.KV_FP8, I.KV_FP8_NOPE_UE8M0]
 FMT_IDS = ["bf16", "fp8", "v4fp8"]
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_cache_policies_give_identical_results(fmt, splits):
+    """The cache policy changes only the cache hints of the row loads and result stores: every policy
+    gives the same bits, and those match the oracle."""
+    inp = I.small_inputs(batch=3, q_len=1, topk=300, seq_len=900, kv_format=fmt, seed=150 + fmt)
+    runs = [run_gpu(inp, force_splits=splits, cache_policy=pol) for pol in (1, 2, 3, 4)]
+    for out, lse in runs[1:]:
+        assert torch.equal(out, runs[0][0]) and torch.equal(lse, runs[0][1])
+    ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
+    check(runs[0][0], runs[0][1], ref_o, ref_l, f"fmt{fmt} S={splits} policies")
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
