@@ -85,7 +85,8 @@ typedef enum {
 /* Cache policy of the partial-attention kernel's memory traffic.  "Streaming"
  * marks the accesses non-temporal (the nt bit of gfx950 loads and stores: no
  * reuse expected, so the caches keep other data).  Rows: the gathered latent
- * rows; out: the per-part results (or the output with one part).  The
+ * rows; out: the per-part results (or the output with one part), which the
+ * combine kernel of smla_decode_run then reads with non-temporal loads.  The
  * arithmetic, and so every result, is the same under every policy.
  * SMLA_CACHE_AUTO lets the plan choose from the problem shape: streaming rows
  * when the call may gather at least 64 MiB, streaming outputs when it writes

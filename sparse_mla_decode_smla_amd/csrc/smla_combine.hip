@@ -45,13 +45,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Adds parts s_first .. s_first + NB - 1 (weights in lanes w_lane .. w_lane + NB - 1
-// of `w`) to the accumulators; all NB loads are issued before any is used.
-template <int NB>
+// of `w`) to the accumulators; all NB loads are issued before any is used (as
+// non-temporal loads when NT: the parts were streamed out and are read once).
+template <int NB, bool NT>
 __device__ __forceinline__ void add_parts(const uint16_t* base, int64_t part_stride, int s_first, int w_lane, float w,
                                           f32x4& acc0, f32x4& acc1) {
     bf16x8 v[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) v[j] = *(const bf16x8*)(base + (int64_t)(s_first + j) * part_stride);
+    for (int j = 0; j < NB; ++j) {
+        const bf16x8* src = (const bf16x8*)(base + (int64_t)(s_first + j) * part_stride);
+        v[j] = NT ? __builtin_nontemporal_load(src) : *src;
+    }
     // (the scheduler would otherwise interleave loads and uses of a 16-part
     // batch, one round trip per part, to keep the kernel under 64 VGPRs)
     __builtin_amdgcn_sched_barrier(0);
@@ -76,7 +80,7 @@ __device__ __forceinline__ void add_parts(const uint16_t* base, int64_t part_str
 // per pair; wave w adds the parts of the w-th of NW contiguous ranges and
 // waves 1..NW-1 hand their sums to wave 0 through LDS.  Several waves per pair
 // put more loads in flight when there are few pairs (small batch).
-template <int NW>
+template <int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __restrict__ part_out,
                                                           const float* __restrict__ part_lse, int num_splits,
                                                           int64_t pairs, uint16_t* __restrict__ out,
@@ -101,10 +105,10 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __rest
             const float wt = l == -INFINITY ? 0.f : expf(l - total);  // weight of part `lane`
             const int n = hi - lo;
             int j0 = 0;
-            for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
-            if (j0 + 8 <= n) { add_parts<8>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 8; }
-            if (j0 + 4 <= n) { add_parts<4>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 4; }
-            for (; j0 < n; ++j0) add_parts<1>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
+            for (; j0 + 16 <= n; j0 += 16) add_parts<16, NT>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
+            if (j0 + 8 <= n) { add_parts<8, NT>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 8; }
+            if (j0 + 4 <= n) { add_parts<4, NT>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1); j0 += 4; }
+            for (; j0 < n; ++j0) add_parts<1, NT>(base, part_stride, lo + j0, lo + j0, wt, acc0, acc1);
         }
     } else {
         // ---- weights: M, z and lse over all parts (lane i holds parts i, i+64, ...), in every wave
@@ -129,10 +133,10 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __rest
                 }
                 const int n = min(64, hi - s0);
                 int j0 = 0;
-                for (; j0 + 16 <= n; j0 += 16) add_parts<16>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
-                if (j0 + 8 <= n) { add_parts<8>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
-                if (j0 + 4 <= n) { add_parts<4>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
-                for (; j0 < n; ++j0) add_parts<1>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+                for (; j0 + 16 <= n; j0 += 16) add_parts<16, NT>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
+                if (j0 + 8 <= n) { add_parts<8, NT>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 8; }
+                if (j0 + 4 <= n) { add_parts<4, NT>(base, part_stride, s0 + j0, j0, wt, acc0, acc1); j0 += 4; }
+                for (; j0 < n; ++j0) add_parts<1, NT>(base, part_stride, s0 + j0, j0, wt, acc0, acc1);
             }
         }
     }
@@ -161,16 +165,27 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __rest
 
 }  // namespace
 
-smla_status_t launch_combine(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs,
-                             void* out, float* lse, hipStream_t stream) {
-    if (pairs == 0) return SMLA_OK;
+template <bool NT>
+void launch_combine_nt(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs, void* out,
+                       float* lse, hipStream_t stream) {
     // few pairs (small batch): four waves per pair so that more part loads are in flight
     if (pairs <= 512)
-        hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)pairs), dim3(256), 0, stream, part_out, part_lse,
+        hipLaunchKernelGGL((combine_kernel<4, NT>), dim3((unsigned)pairs), dim3(256), 0, stream, part_out, part_lse,
                            num_splits, pairs, (uint16_t*)out, lse);
     else
-        hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)pairs), dim3(64), 0, stream, part_out, part_lse,
+        hipLaunchKernelGGL((combine_kernel<1, NT>), dim3((unsigned)pairs), dim3(64), 0, stream, part_out, part_lse,
                            num_splits, pairs, (uint16_t*)out, lse);
+}
+
+// stream_parts: the parts were written with non-temporal stores (they are
+// then read with non-temporal loads too).
+smla_status_t launch_combine(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs,
+                             void* out, float* lse, hipStream_t stream, bool stream_parts) {
+    if (pairs == 0) return SMLA_OK;
+    if (stream_parts)
+        launch_combine_nt<true>(part_out, part_lse, num_splits, pairs, out, lse, stream);
+    else
+        launch_combine_nt<false>(part_out, part_lse, num_splits, pairs, out, lse, stream);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -187,5 +202,6 @@ extern "C" smla_status_t smla_combine(const void* part_out, const float* part_ls
     if (!part_out || !part_lse || !out || !lse) return SMLA_ERR_INVALID_ARG;
     if (((uintptr_t)part_out & 15) != 0 || ((uintptr_t)out & 15) != 0) return SMLA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return smla::launch_combine((const uint16_t*)part_out, part_lse, num_splits, pairs, out, lse, (hipStream_t)stream);
+    return smla::launch_combine((const uint16_t*)part_out, part_lse, num_splits, pairs, out, lse, (hipStream_t)stream,
+                                false);
 }

@@ -44,7 +44,7 @@
 namespace smla {
 
 smla_status_t launch_combine(const uint16_t* part_out, const float* part_lse, int num_splits, int64_t pairs,
-                             void* out, float* lse, hipStream_t stream);
+                             void* out, float* lse, hipStream_t stream, bool stream_parts);
 
 namespace {
 
@@ -1137,5 +1137,5 @@ extern "C" smla_status_t smla_decode_run(const smla_plan_t* plan, const void* q,
                                        &args);
     if (st != SMLA_OK || plan->rows == 0 || plan->num_splits == 1) return st;
     return launch_combine(args.part_out, args.part_lse, plan->num_splits, (int64_t)plan->rows * kHeads, out, lse,
-                          (hipStream_t)stream);
+                          (hipStream_t)stream, args.stream_out != 0);
 }
