@@ -89,8 +89,9 @@ typedef enum {
  * combine kernel of smla_decode_run then reads with non-temporal loads.  The
  * arithmetic, and so every result, is the same under every policy.
  * SMLA_CACHE_AUTO lets the plan choose from the problem shape: streaming rows
- * when the call may gather at least 64 MiB, streaming outputs when it writes
- * at least 4 MiB (thresholds set by measurement on MI355X). */
+ * and outputs when the call writes at least 4 MiB of results, streaming rows
+ * alone when it may gather at least 64 MiB, else cached (thresholds set by
+ * measurement on MI355X). */
 typedef enum {
     SMLA_CACHE_AUTO = 0,
     SMLA_CACHE_CACHED = 1,          /* rows and outputs through the caches as ordinary accesses */

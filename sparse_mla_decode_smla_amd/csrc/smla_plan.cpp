@@ -70,22 +70,20 @@ double estimate_us(const smla_problem_t& p, int rows, int tiles, int S, int cus)
     return t;
 }
 
-// Streaming (non-temporal) row gathers when a call may gather 64 MiB or more,
-// streaming outputs when it writes 4 MiB or more.  Measured on MI355X with
-// the benchmark's workloads (cold cache, HIP graphs): streaming rows took the
-// batch-64 top-2048 bf16 call from 41.4 to 39.1 us (with streaming outputs)
-// and the fp8 batch-128 call from 109.6 to 106.1 us, but slowed calls that
-// gather 38 MB or less (batch 16: 21.7 to 23.2 us); streaming outputs helped
-// once a call writes 8 MB or more (batch 16: 21.7 to 21.2 us) and slowed the
-// batch-1 calls, which write 1 to 2 MB (13.6 to 14.0 us).
+// Streaming (non-temporal) outputs when a call writes 4 MiB or more of
+// results, and then streaming row gathers too; streaming row gathers alone
+// when it may gather 64 MiB or more.  Measured on MI355X with the benchmark's
+// workloads (cold cache, HIP graphs, us per call, cached -> chosen):
+// batch 16 bf16 21.7 -> 20.9, batch 64 bf16 41.5 -> 39.1, fp8 batch 128
+// 111.7 -> 109.6, pages' layout batch 64 24.1 -> 22.3; the batch-1 calls,
+// which write 1 to 2 MB, were as fast or faster with cached accesses.
+// Streaming rows with cached outputs made the batch-16 call slower (23.2 us):
+// the combine kernel then reads the parts with ordinary loads.
 int choose_cache_policy(const smla_problem_t& p, int rows, int splits) {
     const double gathered = (double)rows * p.topk * smla::gathered_bytes_per_token(p.kv_format);
     const double written = (double)rows * splits * smla::kHeads * smla::kDv * 2.0;
-    const bool rows_stream = gathered >= 64.0 * (1 << 20);
-    const bool out_stream = written >= 4.0 * (1 << 20);
-    if (rows_stream && out_stream) return SMLA_CACHE_STREAM_BOTH;
-    if (rows_stream) return SMLA_CACHE_STREAM_ROWS;
-    if (out_stream) return SMLA_CACHE_STREAM_OUT;
+    if (written >= 4.0 * (1 << 20)) return SMLA_CACHE_STREAM_BOTH;
+    if (gathered >= 64.0 * (1 << 20)) return SMLA_CACHE_STREAM_ROWS;
     return SMLA_CACHE_CACHED;
 }
 

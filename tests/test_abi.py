@@ -64,13 +64,14 @@ PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_pa
                   "b64_topk512_n8192_paged_v4fp8": 4}
 
 
-# cache policies the plan chooses automatically: streaming rows from 64 MiB of gathered rows (upper
-# bound rows * topk * row bytes), streaming outputs from 4 MiB of results written by the partial kernel
+# cache policies the plan chooses automatically: streaming rows and outputs from 4 MiB of results written
+# by the partial kernel, streaming rows alone from 64 MiB of gathered rows (upper bound rows * topk * row
+# bytes), else cached
 PLANNED_POLICY = {"b1_topk512_n4096_contiguous_bf16": B.CACHE_CACHED, "b1_topk2048_n32768_paged_bf16": B.CACHE_CACHED,
-                  "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_OUT,
+                  "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_BOTH,
                   "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_BOTH,
                   "b128_q2_topk2048_n65536_paged_fp8": B.CACHE_STREAM_BOTH,
-                  "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_OUT}
+                  "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_BOTH}
 
 
 @pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
@@ -92,7 +93,9 @@ def test_plan_cache_policy_thresholds():
     tiny = B.decode_plan(2, 1, 2048, 64, num_cus=256, force_splits=1)      # 4.7 MB rows, 128 KiB out
     assert tiny.cache_policy == B.CACHE_CACHED
     out = B.decode_plan(64, 1, 32, 64, num_cus=256, force_splits=1)        # 2.4 MB rows, 4 MiB out
-    assert out.cache_policy == B.CACHE_STREAM_OUT
+    assert out.cache_policy == B.CACHE_STREAM_BOTH
+    out_below = B.decode_plan(63, 1, 32, 64, num_cus=256, force_splits=1)  # 4 MiB - 64 KiB out
+    assert out_below.cache_policy == B.CACHE_CACHED
     for bad in (-1, 5):
         with pytest.raises(B.SmlaError):
             B.decode_plan(1, 1, 64, 4, num_cus=256, cache_policy=bad)
