@@ -339,8 +339,9 @@ def _graph_timer(torch, stream, K, flush_buf=None):
 
 
 def gather_probe(nbytes: int = 16 << 30, ntiles: int = 64, reps: int = 3) -> int:
-    """Random 1152-byte rows gathered into LDS by LDS-DMA with four instruction patterns (libsmla_probe.so,
-    no compute), at 128 and 256 workgroups; one JSON line per (mode, workgroups) with the best of `reps`."""
+    """Random 1152-byte rows gathered into LDS by LDS-DMA with four instruction patterns, and the kernel's
+    pattern with non-temporal loads (libsmla_probe.so, no compute), at 128, 192 and 256 workgroups; one JSON
+    line per (mode, workgroups) with the best of `reps`."""
     import ctypes
     import numpy as np
     import torch
@@ -354,12 +355,13 @@ def gather_probe(nbytes: int = 16 << 30, ntiles: int = 64, reps: int = 3) -> int
     buf = torch.ones(nrows * 1152, dtype=torch.uint8, device=dev)
     rng = np.random.default_rng(0)
     names = {0: "8 rows x 128 B, 8 lanes per row (band-major, as the kernel)", 1: "1 row x 1024 B (row-major)",
-             2: "8 rows x 128 B, lanes by half band", 3: "8 rows x 128 B, lanes interleaved by row"}
-    for grid in (128, 256):
+             2: "8 rows x 128 B, lanes by half band", 3: "8 rows x 128 B, lanes interleaved by row",
+             4: "band-major, non-temporal loads (nt)"}
+    for grid in (128, 192, 256):
         rows = torch.from_numpy(rng.integers(0, nrows, size=grid * ntiles * 32, dtype=np.int32)).to(dev)
         sink = torch.empty(grid, dtype=torch.int32, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
-        for mode in range(4):
+        for mode in range(5):
             best = float("inf")
             for _ in range(reps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

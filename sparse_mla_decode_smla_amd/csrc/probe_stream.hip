@@ -10,13 +10,16 @@
 // (global_load_lds_dwordx4), as the decode kernel gathers latent rows, with
 // different spreads of one instruction's 64 lanes over rows.  Four issuing
 // waves per workgroup, each taking 8 rows per tile into its own ring of 4
-// stages with 3 tiles in flight, no compute.  Modes (the 64 lanes of one
+// stages with 3 tiles in flight, no compute; the workgroup's row numbers are
+// first copied into LDS (as the decode kernel holds its row table), so that
+// no global load of a row number waits behind the gathers in flight.  Modes (the 64 lanes of one
 // 1 KB instruction): 0 = 8 rows x 128 bytes, 8 consecutive lanes per row (the
 // kernel's band-major gather); 1 = 1 row x 1024 bytes (row-major; a ninth
 // instruction takes the 8 rows' last 128 bytes); 2 = the same 8 rows x 128
 // bytes as 0, lanes ordered by half band (lane l takes bytes
 // 64 (l / 32) + 16 (l % 4) of row (l / 4) % 8); 3 = the same bytes, lanes
-// interleaved by row (lane l takes chunk l / 8 of row l % 8).
+// interleaved by row (lane l takes chunk l / 8 of row l % 8); 4 = mode 0 with
+// the loads marked non-temporal (the nt bit).
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -28,10 +31,16 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
+    if (NT)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory", "m0");
 }
 #pragma clang diagnostic pop
 template <int N>
@@ -40,6 +49,8 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kRow = 1152, kTileRows = 32, kStages = 4, kWaveStage = 8 * kRow;  // 9216 bytes
+constexpr int kRowTab = 4 * kStages * kWaveStage;  // LDS offset of the row numbers
+constexpr int kMaxTiles = 64;                      // row numbers held: kMaxTiles * kTileRows
 
 template <int MODE>
 __global__ __launch_bounds__(256) void gather_kernel(const unsigned char* __restrict__ buf,
@@ -48,7 +59,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const unsigned char* __rest
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const unsigned base = (unsigned)(uintptr_t)lds + (unsigned)(w * kStages * kWaveStage);
-    const int* my = rows + (size_t)blockIdx.x * ntiles * kTileRows + 8 * w;
+    int* tab = (int*)(lds + kRowTab);
+    for (int i = threadIdx.x; i < ntiles * kTileRows; i += blockDim.x)
+        tab[i] = rows[(size_t)blockIdx.x * ntiles * kTileRows + i];
+    __syncthreads();
+    const int* my = tab + 8 * w;
     for (int t = 0; t < ntiles; ++t) {
         const unsigned st = base + (unsigned)((t % kStages) * kWaveStage);
         if (MODE == 1) {
@@ -57,12 +72,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const unsigned char* __rest
             dma16(buf + (size_t)my[t * kTileRows + (lane >> 3)] * kRow + 1024 + (lane & 7) * 16, st + 8 * 1024);
         } else {
             int r, off;
-            if (MODE == 0) { r = lane >> 3; off = (lane & 7) * 16; }
+            if (MODE == 0 || MODE == 4) { r = lane >> 3; off = (lane & 7) * 16; }
             else if (MODE == 2) { r = (lane >> 2) & 7; off = (lane >> 5) * 64 + (lane & 3) * 16; }
             else { r = lane & 7; off = (lane >> 3) * 16; }
             const unsigned char* src = buf + (size_t)my[t * kTileRows + r] * kRow + off;
 #pragma unroll
-            for (int b = 0; b < 9; ++b) dma16(src + b * 128, st + b * 1024);
+            for (int b = 0; b < 9; ++b) dma16<MODE == 4>(src + b * 128, st + b * 1024);
         }
         if (t >= kStages - 1) wait_vm<9 * (kStages - 1)>();
     }
@@ -89,15 +104,15 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 }  // namespace
 
-// buf: nrows rows of 1152 bytes; rows: int32 [grid, ntiles, 32] row numbers, each in [0, nrows); sink:
-// grid words.  One launch of `grid` workgroups of 256 threads with 147,456 bytes of LDS.  Returns 0 on a
+// buf: nrows rows of 1152 bytes; rows: int32 [grid, ntiles, 32] row numbers, each in [0, nrows), ntiles <= 64;
+// sink: grid words.  One launch of `grid` workgroups of 256 threads with 155,648 bytes of LDS.  Returns 0 on a
 // successful launch, -1 on bad arguments, else the HIP error.
 extern "C" int smla_probe_gather(const void* buf, const int* rows, int ntiles, int mode, unsigned* sink, int grid,
                                  void* stream) {
-    if (!buf || !rows || !sink || grid <= 0 || ntiles <= 0 || mode < 0 || mode > 3) return -1;
-    const size_t lds = 4 * kStages * kWaveStage;
-    const void* fns[4] = {(const void*)gather_kernel<0>, (const void*)gather_kernel<1>, (const void*)gather_kernel<2>,
-                          (const void*)gather_kernel<3>};
+    if (!buf || !rows || !sink || grid <= 0 || ntiles <= 0 || ntiles > kMaxTiles || mode < 0 || mode > 4) return -1;
+    const size_t lds = kRowTab + 4 * kMaxTiles * kTileRows;
+    const void* fns[5] = {(const void*)gather_kernel<0>, (const void*)gather_kernel<1>, (const void*)gather_kernel<2>,
+                          (const void*)gather_kernel<3>, (const void*)gather_kernel<4>};
     hipError_t e = hipFuncSetAttribute(fns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
     const unsigned char* b = (const unsigned char*)buf;
@@ -106,6 +121,7 @@ extern "C" int smla_probe_gather(const void* buf, const int* rows, int ntiles, i
         case 0: hipLaunchKernelGGL(gather_kernel<0>, dim3(grid), dim3(256), lds, st, b, rows, ntiles, sink); break;
         case 1: hipLaunchKernelGGL(gather_kernel<1>, dim3(grid), dim3(256), lds, st, b, rows, ntiles, sink); break;
         case 2: hipLaunchKernelGGL(gather_kernel<2>, dim3(grid), dim3(256), lds, st, b, rows, ntiles, sink); break;
+        case 4: hipLaunchKernelGGL(gather_kernel<4>, dim3(grid), dim3(256), lds, st, b, rows, ntiles, sink); break;
         default: hipLaunchKernelGGL(gather_kernel<3>, dim3(grid), dim3(256), lds, st, b, rows, ntiles, sink); break;
     }
     return (int)hipGetLastError();
