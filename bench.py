@@ -380,6 +380,44 @@ def gather_probe(nbytes: int = 16 << 30, ntiles: int = 64, reps: int = 3) -> int
     return 0
 
 
+def launch_probe(K: int = 200) -> int:
+    """Time of one kernel node in a HIP graph of K back-to-back launches of an almost empty kernel
+    (libsmla_probe.so: thread 0 of each workgroup stores one word): the floor that every launch of the
+    decode path pays.  One JSON line per (workgroups, threads), the best of five replays."""
+    import ctypes
+    import torch
+    from sparse_mla_decode_smla_amd import build as Bd
+    lib = ctypes.CDLL(Bd.PROBE_PATH)
+    lib.smla_probe_empty.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p]
+    lib.smla_probe_empty.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    for grid, threads in ((1, 64), (64, 256), (256, 512)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(K):
+                    rc = lib.smla_probe_empty(sink.data_ptr(), grid, threads, i, stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"launch probe failed: {rc}")
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / K)
+        print(json.dumps({"launch_probe": "graph of back-to-back almost empty kernels", "workgroups": grid,
+                          "threads": threads, "us_per_kernel_node": round(best, 3)}), flush=True)
+    return 0
+
+
 def stream_read_gbs(torch, dev, nbytes: int = 4 << 30, grid: int = 8192) -> tuple[float, str]:
     """Measured read bandwidth of a plain streaming kernel (libsmla_probe.so: one pass of 16-byte
     non-temporal loads over nbytes), the best of five timed calls: a second denominator next to the
@@ -519,6 +557,8 @@ def main() -> int:
                     help="cache hints of the row gathers and result stores (auto: the plan's choice)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain streaming kernel of known size (counter calibration)")
+    ap.add_argument("--launch-probe", action="store_true",
+                    help="time one node of a HIP graph of almost empty kernels (the per-launch floor)")
     ap.add_argument("--gather-probe", action="store_true",
                     help="run only the row-gather probe (LDS-DMA instruction patterns, no compute)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -542,6 +582,8 @@ def main() -> int:
         return copy_probe()
     if args.gather_probe:
         return gather_probe()
+    if args.launch_probe:
+        return launch_probe()
 
     import numpy as np
     import torch

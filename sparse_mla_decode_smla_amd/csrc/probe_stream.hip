@@ -86,6 +86,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const unsigned char* __rest
     if (threadIdx.x == 0) sink[blockIdx.x] = *(volatile unsigned*)lds;
 }
 
+// Launch floor: a kernel that does almost nothing (thread 0 of each
+// workgroup stores one word), for timing a graph of back-to-back launches.
+__global__ void empty_kernel(unsigned* __restrict__ sink, unsigned v) {
+    if (threadIdx.x == 0) sink[blockIdx.x] = v;
+}
+
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
                                                           unsigned* __restrict__ sink) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -134,5 +140,13 @@ extern "C" int smla_probe_stream_read(const void* buf, size_t bytes, unsigned* s
     if (!buf || !sink || grid <= 0 || (bytes & 15) || ((uintptr_t)buf & 15)) return -1;
     hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)buf,
                        bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+// sink: device buffer of at least grid unsigned words; 1 <= threads <= 1024.  Enqueues one launch of
+// `grid` workgroups of `threads` threads on `stream`.  Returns 0, -1 on bad arguments, else the HIP error.
+extern "C" int smla_probe_empty(unsigned* sink, int grid, int threads, unsigned value, void* stream) {
+    if (!sink || grid <= 0 || threads <= 0 || threads > 1024) return -1;
+    hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream, sink, value);
     return (int)hipGetLastError();
 }
