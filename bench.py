@@ -301,7 +301,7 @@ def _median(xs):
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
-def _graph_timer(torch, stream, K, flush_buf=None):
+def _graph_timer(torch, stream, K, flush_buf=None, warm_seconds=WARM_SECONDS):
     """capture(fn) records fn(0..K-1) in one graph; time_graph(g, cold) replays it N_REPLAYS times, each
     timed with events on `stream` (with cold, `flush_buf` is read on that stream first), and
     returns (median us per step, [us per step of each replay])."""
@@ -316,11 +316,17 @@ def _graph_timer(torch, stream, K, flush_buf=None):
 
     def time_graph(g, cold: bool = True):
         # (a written flush would leave dirty lines whose write-back lands in the timed replay)
-        # untimed replays for at least WARM_SECONDS first: the clock settles under sustained load
+        # untimed replays for at least WARM_SECONDS first, each run exactly as a timed one (flush, then
+        # replay): the clock and the translation caches settle under the same alternation of the
+        # flush and the steps.  (With back-to-back replays alone, the first timed replays of the
+        # compute-bound fp8 workload ran 10-25% slower at 20 steps per replay.)
         t0 = time.perf_counter()
         n = 0
-        while n < 1 or (time.perf_counter() - t0 < WARM_SECONDS and n < 1000):
-            g.replay()
+        while n < 1 or (time.perf_counter() - t0 < warm_seconds and n < 1000):
+            with torch.cuda.stream(stream):
+                if cold and flush_buf is not None:
+                    torch.sum(flush_buf)
+                g.replay()
             torch.cuda.synchronize()
             n += 1
         per = []
@@ -487,7 +493,7 @@ def bench_indexer(args) -> int:
     K = args.steps
     stream = torch.cuda.Stream(device=dev)
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    capture, time_graph = _graph_timer(torch, stream, K, flush_buf)
+    capture, time_graph = _graph_timer(torch, stream, K, flush_buf, args.warm_seconds)
     g = capture(step)
     g.replay()
     torch.cuda.synchronize()
@@ -550,6 +556,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="untimed replays of each graph before its timed replays (clock and caches settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-splits", type=int, default=0, help="override the planned split count (sweeps)")
     ap.add_argument("--cache-policy", default="auto", choices=["auto", "cached", "stream-rows", "stream-out",
@@ -638,7 +646,7 @@ def main() -> int:
     K = args.steps
     stream = torch.cuda.Stream(device=dev)
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    capture, time_graph = _graph_timer(torch, stream, K, flush_buf)
+    capture, time_graph = _graph_timer(torch, stream, K, flush_buf, args.warm_seconds)
 
     graph = capture(step)
     graph.replay()
@@ -705,6 +713,7 @@ def main() -> int:
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_call_eager": round(eager_us, 3),
         "kernels_us": {"partial": round(partial_us, 3), "combine": round(combine_us, 3)},
+        "partial_us_replays": [round(x, 3) for x in partial_reps],
         "hot": {"us_per_call": round(hot_call_us, 3), "partial_us": round(hot_partial_us, 3),
                 "note": "every step on the same cache copy, no flush: rows served from the caches"},
         "stream_read": {"gbs": round(read_gbs, 1), "how": read_how,
