@@ -135,8 +135,9 @@ typedef struct {
 } smla_plan_t;
 
 /*
- * Fill *plan_out for *prob: the split count S, the part length and the
- * workspace size, a pure function of the problem shape and the CU count, so
+ * Fill *plan_out for *prob: the split count S, the part length, the
+ * workspace size and the cache policy, a pure function of the problem shape
+ * and the CU count, so
  * that a launch captured for a batch bucket stays valid ("The Moment of
  * Truth: Analyzing a Custom MMA Kernel's Performance on Blackwell GPUs",
  * "The Split-K Solution: Reasoning About the Fix": split count and scratch
@@ -144,7 +145,8 @@ typedef struct {
  * program per row leaves most of the GPU idle at small batch).  Host only;
  * touches the device only when prob->num_cus == 0 (to read the current
  * device's CU count).
- * Returns SMLA_ERR_INVALID_ARG for null pointers or negative sizes,
+ * Returns SMLA_ERR_INVALID_ARG for null pointers, negative sizes or a
+ * cache_policy outside smla_cache_policy_t,
  * SMLA_ERR_UNSUPPORTED for shapes outside the supported set,
  * SMLA_ERR_DEVICE if the CU count cannot be read.
  */
