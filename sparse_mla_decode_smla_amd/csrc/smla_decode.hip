@@ -4,9 +4,10 @@
 // One workgroup handles one query row (b, s), all 64 heads, and one part of
 // that row's top-k list.  Every selected latent row is gathered from the
 // paged cache into LDS once and read from there by all eight waves: QK
-// waves 0..3 (wave w owns heads [16w, 16w + 16)) and PV waves 4..7 (wave
-// 4 + p owns value dims [128p, 128p + 128) and issues a quarter of the
-// gathers).  This is the head batching of "The MMA Sparse-MLA
+// waves 0..3 (wave w owns heads [16w, 16w + 16); for fp8 rows waves 2c and
+// 2c + 1 share heads [32c, 32c + 32) and split each tile's tokens) and PV
+// waves 4..7 (wave 4 + p owns value dims [128p, 128p + 128) and issues a
+// quarter of the gathers).  This is the head batching of "The MMA Sparse-MLA
 // Decode Kernel: A Deep Dive into AI Inference Optimization on Blackwell
 // GPUs" (Agent Reasoning, "Design Decisions" 1 and "Memory Budgeting"), here
 // with all 64 heads in one workgroup since a gfx950 CU has 160 KB of LDS.
@@ -107,6 +108,27 @@ __device__ __forceinline__ void lds_dma4(const void* src, unsigned lds_base) {
 }
 #pragma clang diagnostic pop
 
+// Lane swaps between the halves of a wave (v_permlane32_swap: lanes 32..63
+// of a with lanes 0..31 of b) and between odd and even rows of 16 lanes
+// (v_permlane16_swap: rows 1, 3 of a with rows 0, 2 of b).  With a = b = x,
+// max(a, b) or a + b afterwards reduces x over lanes l and l ^ 32 (l ^ 16).
+// (The results are copied out of the returned pair before the bit cast: a
+// bit cast of a vector element expression reads element 0.)
+__device__ __forceinline__ void lane_swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void lane_swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -205,6 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int AUX_ALPHA = aux_alpha_offset(FMT);
     constexpr int AUX_FLAG = aux_flag_offset(FMT);
     constexpr int AUX_DENOM = aux_denom_offset(FMT);
+    constexpr int AUX_SWAP = aux_swap_offset(FMT);
     lds_u8* aux = lds + NST * STAGE;
     lds_u8* rowtab = aux + aux_bytes(FMT);  // int32 per token of this part: physical row or -1
 
@@ -442,310 +465,556 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // of tile k into registers and wait for tile k+1 to land.  NST - 2 tiles
     // beyond the next one are in flight while a tile is computed.
     if (wave < 4) {
-        // =================== QK waves: heads [16q, 16q + 16) ===================
-        const int q = wave;
-        const int head = 16 * q + i16;
-        // Q of `head` as the B operand of S^T = K . Q^T (8 dims of k-step kk per
-        // lane); for fp8 rows the c_kv dims of k-steps 2p and 2p+1 inside a
-        // 128-group are the two halves of one 16-byte run, so one LDS read
-        // feeds two k-steps.
-        // (v4 rows: the 16-byte run of nope group u feeds k-steps 2u and 2u+1;
-        // k-steps 14 and 15 are the rope values.)
-        constexpr int NQ = FMT == 2 ? 16 : 18;
-        bf16x8 qreg[NQ];
-        {
-            const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * DQK;
+        if constexpr (FMT == 1) {
+            // ====== QK waves: wave 2c + h, heads [32c, 32c + 32), tokens [16h, 16h + 16) of each tile ======
+            // The two waves of pair c own the same 32 heads (16-head blocks 2c and
+            // 2c + 1) and split each tile's tokens between them: every K operand
+            // read from LDS then feeds two MFMAs, one per head block, and every
+            // fp8 code is widened by two waves rather than four.  The pair agrees
+            // on the reference maximum of each head by swapping per-head values
+            // through LDS once a step (`swap_post`, `swap_wait`).  Head block A of
+            // wave 2c + h is block 2c + h, its block B the partner's block A.
+            const int hp = wave >> 1;    // head pair
+            const int half = wave & 1;   // token half
+            const int headA = 16 * (2 * hp + half) + i16, headB = 16 * (2 * hp + 1 - half) + i16;
+            // Q of headA / headB as the B operand of S^T = K . Q^T (8 dims of
+            // k-step kk per lane); for fp8 rows the c_kv dims of k-steps 2p and
+            // 2p+1 inside a 128-group are the two halves of one 16-byte run, so
+            // one LDS read feeds two k-steps.
+            // Each wave loads block A from HBM before T1, as every QK wave loads
+            // one block, and hands it to its partner through the stages of tiles
+            // 2 .. (and the P buffers), which are empty until P0: loading both
+            // blocks from HBM made the first-touch loads of the second block (whose
+            // address translations miss) hold up the first tiles' gathers.
+            constexpr int NQ = 18;
+            bf16x8 qa[NQ], qb[NQ];
+            {
+                const uint16_t* const qh = a.q + ((int64_t)r * kHeads + headA) * DQK;
 #pragma unroll
-            for (int kk = 0; kk < NQ; ++kk) {
-                int d;
-                if (FMT == 2)
-                    d = kk < 14 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : kNopeV4 + 32 * (kk - 14) + 8 * g;
-                else if (FMT == 0 || kk >= 16)
-                    d = 32 * kk + 8 * g;
-                else
-                    d = 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
-                qreg[kk] = *(const bf16x8*)(qh + d);
+                for (int kk = 0; kk < NQ; ++kk) {
+                    const int d = kk >= 16 ? 32 * kk + 8 * g : 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
+                    qa[kk] = *(const bf16x8*)(qh + d);
+                }
             }
-        }
-        __syncthreads();  // T1
-        __syncthreads();  // B0
-        wait_vmcnt<0>();
+            // this wave's slot in the swap area: 16-byte records {headA, headB, seq, seq}
+            // per head of a block (read by the partner only after T1)
+            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+            volatile lds_f32x4* const swap_mine = (volatile lds_f32x4*)(aux + AUX_SWAP) + 16 * wave + i16;
+            const volatile lds_f32x4* const swap_part = (const volatile lds_f32x4*)(aux + AUX_SWAP) + 16 * (wave ^ 1) + i16;
+            if (g == 0) *swap_mine = f32x4{0.f, 0.f, 0.f, 0.f};
+            // Per-head swap with the partner wave: this lane's values for headA and
+            // headB go out (lanes of group 0) in one 16-byte record tagged with the
+            // step count `seq` (written by one instruction, so a record whose tags
+            // read `seq` holds this step's values), and the partner's record is
+            // read until it carries `seq`.  The partner posts its record in the
+            // same step without waiting on this wave, so the wait ends.  One record
+            // suffices: the next one is written after the step's barrier, which the
+            // partner passes only after reading this one.
+            // (vector elements are copied to scalars before any bit cast: a bit
+            // cast of an element expression read element 0)
+            auto swap_post = [&](float va, float vb, int seq) {
+                const float tag = __builtin_bit_cast(float, seq);
+                if (g == 0) *swap_mine = f32x4{va, vb, tag, tag};
+            };
+            auto swap_wait = [&](int seq, float& pa, float& pb) {
+                f32x4 o = *swap_part;
+                while (true) {
+                    const float t0 = o[2], t1 = o[3];
+                    if (__all(__builtin_bit_cast(int, t0) == seq && __builtin_bit_cast(int, t1) == seq)) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    o = *swap_part;
+                }
+                pa = o[1];  // the partner's block B is this wave's block A
+                pb = o[0];
+            };
+            // sum or maximum over the four lanes of a head (lane groups g), by lane swaps
+            auto head_max = [](float x) {
+                float u = x, v = x;
+                lane_swap32(u, v);
+                x = fmaxf(u, v);
+                u = x;
+                v = x;
+                lane_swap16(u, v);
+                return fmaxf(u, v);
+            };
+            auto head_sum = [](float x) {
+                float u = x, v = x;
+                lane_swap32(u, v);
+                x = u + v;
+                u = x;
+                v = x;
+                lane_swap16(u, v);
+                return u + v;
+            };
+            __syncthreads();  // T1
+            __syncthreads();  // B0
+            wait_vmcnt<0>();
+            static_assert(2 * STAGE + 4 * NQ * 1024 <= NST * STAGE + 2 * PBUF && NST >= 3,
+                          "the query hand-over area exceeds the stages of tiles 2.. and the P buffers");
+            {
+                // ---- the query hand-over: this wave's block A is the partner's block
+                // B.  (The hand-over and the swaps share the records: tag 1 here,
+                // k + 2 for the maxima of tile k, ntiles + 2 for the denominators.)
+                typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+                lds_bf16x8* const xq = (lds_bf16x8*)(lds + 2 * STAGE) + lane;
 #pragma unroll
-        for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
-
-        // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
-        // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
-        const int tokA0 = i16, tokA1 = 16 + i16;
-        const int tokC0 = 4 * g, tokC1 = 16 + 4 * g;
-        int qk0[2], qk1[2];
+                for (int kk = 0; kk < NQ; ++kk) xq[(wave * NQ + kk) * 64] = qa[kk];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // block A is in LDS before its tag
+                float d0, d1;
+                swap_post(0.f, 0.f, 1);
+                swap_wait(1, d0, d1);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz(tokA0)) << 4);
-            qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz(tokA1)) << 4);
-        }
-        // v4: this lane's chunk of the half band (rope values 32 + 8g .. 32 + 8g + 7)
-        const int qh0 = HALF_OFF + tokA0 * 64 + ((g ^ swz4(tokA0)) << 4);
-        const int qh1 = HALF_OFF + tokA1 * 64 + ((g ^ swz4(tokA1)) << 4);
-        // P slot of this lane: (block q, group g, lane i16): its 8 weights are
-        // the k-slots 8g .. 8g + 7 of the PV B operand, i.e. tokens
-        // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
-        lds_u8* const p_mine = aux + ((q * 4 + g) * 16 + i16) * 16;  // + buffer (+ group copy for fp8)
-
-        // Online softmax of `head`, base 2.  Weights are taken against a
-        // reference maximum m_ref, set at the first tile with a valid token;
-        // it is raised only when a tile's maximum exceeds it by more than
-        // kMaxRise (weights up to 2^kMaxRise stay finite in fp32 and bf16), and
-        // then the denominator here and the output accumulators of the PV waves
-        // are rescaled by alpha = 2^(old - new).
-        constexpr float kMaxRise = 32.f;
-        float m_ref = -INFINITY;  // the same in the four lanes of the head
-        float l_run = 0.f;        // this lane's share of the denominator
-        bool ref_set = false;     // the same in every lane of the wave
-        const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
-        if (LPT_QK > 0) {
-            for (int t = 0; t < pro; ++t) {
-                const Gather gt = prepare(t);
-#pragma unroll
-                for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+                for (int kk = 0; kk < NQ; ++kk) qb[kk] = xq[((wave ^ 1) * NQ + kk) * 64];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before P0 (tile 2 is gathered there after it)
             }
-            if (ntiles > 0) wait_tiles<LPT_QK>(pro - 1);  // this wave's part of tile 0 has landed
-        }
-        __syncthreads();  // P0
-        for (int k = 0; k <= ntiles; ++k) {
-            int raised = 0;
-            // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
-            if (LPT_QK > 0 && k + NST - 1 < ntiles) {
-                const Gather gt = prepare(k + NST - 1);
 #pragma unroll
-                for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
-            }
-            if (k < ntiles) {
-                const lds_u8* st = lds + (k % NST) * STAGE;
-                const lds_u8* rt = rowtab + 4 * k * kTile;
-                const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
-                const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
+            for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qa[kk]), "+v"(qb[kk]));  // no waits in the loop
 
-                // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
-                f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-                f32x4 sc0[4], sc1[4];  // fp8: sc*[e][grp] = scale of group grp of accumulator token e
-                if (FMT == 0) {
-                    constexpr int PF = 4;  // k-steps of K operands in flight
-                    bf16x8 ka[PF], kb[PF];
+            // K operand row of this lane: token tokA.  Accumulator entry e of a
+            // lane: token tokC + e (the partner's: tokO + e).
+            const int tokA = 16 * half + i16;
+            const int tokC = 16 * half + 4 * g, tokO = 16 * (1 - half) + 4 * g;
+            int qk[2];
 #pragma unroll
-                    for (int kk = 0; kk < PF; ++kk) {
-                        ka[kk] = lds_load<bf16x8>(st + qk0[kk & 1] + (kk >> 1) * kTile * 128);
-                        kb[kk] = lds_load<bf16x8>(st + qk1[kk & 1] + (kk >> 1) * kTile * 128);
-                    }
+            for (int e = 0; e < 2; ++e) qk[e] = tokA * 128 + (((4 * e + g) ^ swz(tokA)) << 4);
+            // P slots of this lane for headA (+ pb_off: headB): (block, group g, lane i16) holds the
+            // k-slots 8g .. 8g + 7 of the PV B operand, i.e. tokens 4g .. 4g + 3 (bytes 0..7) and
+            // 16 + 4g .. 16 + 4g + 3 (bytes 8..15); this wave writes its half.
+            lds_u8* const p_mine = aux + ((((2 * hp + half) * 4 + g) * 16 + i16) * 16) + 8 * half;  // + buffer (+ group copy)
+            const int pb_off = half ? -1024 : 1024;
+
+            // Online softmax of headA and headB, base 2.  Weights are taken against
+            // a reference maximum m_ref, set at the first tile with a valid token;
+            // it is raised only when a tile's maximum exceeds it by more than
+            // kMaxRise (weights up to 2^kMaxRise stay finite in fp32 and bf16), and
+            // then the denominator here and the output accumulators of the PV waves
+            // are rescaled by alpha = 2^(old - new).  Both waves of the pair take
+            // the same decisions from the same maxima.
+            constexpr float kMaxRise = 32.f;
+            float mrA = -INFINITY, mrB = -INFINITY;  // the same in the four lanes of a head and in both waves
+            float lA = 0.f, lB = 0.f;                // this lane's share of the denominators
+            bool ref_set = false;                    // the same in every lane of both waves
+            const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
+            if (LPT_QK > 0) {
+                for (int t = 0; t < pro; ++t) {
+                    const Gather gt = prepare(t);
 #pragma unroll
-                    for (int kk = 0; kk < 18; ++kk) {
-                        const int sl = kk % PF;
-                        s0 = mfma16(ka[sl], qreg[kk], s0);
-                        s1 = mfma16(kb[sl], qreg[kk], s1);
-                        if (kk + PF < 18) {
-                            const int kn = kk + PF;
-                            ka[sl] = lds_load<bf16x8>(st + qk0[kn & 1] + (kn >> 1) * kTile * 128);
-                            kb[sl] = lds_load<bf16x8>(st + qk1[kn & 1] + (kn >> 1) * kTile * 128);
-                        }
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+                    for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+                }
+                if (ntiles > 0) wait_tiles<LPT_QK>(pro - 1);  // this wave's part of tile 0 has landed
+            }
+            __syncthreads();  // P0
+            for (int k = 0; k <= ntiles; ++k) {
+                int raised = 0;
+                // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
+                if (LPT_QK > 0 && k + NST - 1 < ntiles) {
+                    const Gather gt = prepare(k + NST - 1);
 #pragma unroll
-                    for (int i = 0; i < 18 - PF; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
-                } else if (FMT == 2) {
-                    // 9 load units per block: nope groups 0..6 (16 e4m3 values of this
-                    // lane's token, two k-steps, widened with the token's scale of
-                    // that group), then rope values 0..31 and 32..63 (bf16)
-                    constexpr int PF = 3;
-                    u32x4 ka[PF], kb[PF];
-                    auto unit_off = [&](int u, int blk) {
-                        const int* qo = blk == 0 ? qk0 : qk1;
-                        return u < 8 ? qo[u & 1] + (u >> 1) * kTile * 128 : (blk == 0 ? qh0 : qh1);
-                    };
-#pragma unroll
-                    for (int u = 0; u < PF; ++u) {
-                        ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
-                        kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
-                    }
-                    const i32x2 ra = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA0);
-                    const i32x2 rb = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA1);
-#pragma unroll
-                    for (int u = 0; u < 9; ++u) {
-                        const int sl = u % PF;
-                        if (u < 7) {
-                            const float fa = ue8m0_scale(ra, u), fb = ue8m0_scale(rb, u);
-                            s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][0], ka[sl][1], fa), qreg[2 * u], s0);
-                            s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][0], kb[sl][1], fb), qreg[2 * u], s1);
-                            s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][2], ka[sl][3], fa), qreg[2 * u + 1], s0);
-                            s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][2], kb[sl][3], fb), qreg[2 * u + 1], s1);
-                        } else {
-                            s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[7 + u], s0);
-                            s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[7 + u], s1);
-                        }
-                        if (u + PF < 9) {
-                            ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
-                            kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
-                        }
-                    }
-                } else {
-                    // 10 load units per block: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
-                    constexpr int PF = 3;
-                    u32x4 ka[PF], kb[PF];
-                    auto unit_off = [&](int u, int blk) {
-                        const int* qo = blk == 0 ? qk0 : qk1;
-                        return u < 2 ? qo[u] + 4 * kTile * 128 : qo[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
+                    for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+                }
+                if (k < ntiles) {
+                    const lds_u8* st = lds + (k % NST) * STAGE;
+                    const lds_u8* rt = rowtab + 4 * k * kTile;
+                    const i32x4 vc = lds_load<i32x4>(rt + 4 * tokC);  // row entries of this lane's tokens
+                    const i32x4 vo = lds_load<i32x4>(rt + 4 * tokO);  // and of the partner's
+
+                    // ---- S^T = K . Q^T for this half's 16 tokens and the two head blocks
+                    f32x4 sA = f32x4{0.f, 0.f, 0.f, 0.f}, sB = sA;
+                    f32x4 sc[4];  // fp8: sc[e][grp] = scale of group grp of accumulator token tokC + e
+                    {
+                    // 10 load units: rope k-steps 16, 17 (bf16), then c_kv pairs (group, pair)
+                    constexpr int PF = 4;
+                    u32x4 kr[PF];
+                    auto unit_off = [&](int u) {
+                        return u < 2 ? qk[u] + 4 * kTile * 128 : qk[(u - 2) & 1] + ((u - 2) >> 1) * kTile * 128;
                     };
                     const lds_u8* scl = st + NBANDS * kTile * 128;
 #pragma unroll
-                    for (int u = 0; u < PF; ++u) {
-                        ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
-                        kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
-                    }
+                    for (int u = 0; u < PF; ++u) kr[u] = lds_load<u32x4>(st + unit_off(u));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sc0[e] = lds_load<f32x4>(scl + 16 * (tokC0 + e));
-                        sc1[e] = lds_load<f32x4>(scl + 16 * (tokC1 + e));
-                    }
-                    f32x4 p0 = s0, p1 = s0;
+                    for (int e = 0; e < 4; ++e) sc[e] = lds_load<f32x4>(scl + 16 * (tokC + e));
+                    f32x4 pA = sA, pB = sA;
 #pragma unroll
                     for (int u = 0; u < 10; ++u) {
                         const int sl = u % PF;
                         if (u < 2) {
-                            s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[16 + u], s0);
-                            s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[16 + u], s1);
+                            const bf16x8 w = __builtin_bit_cast(bf16x8, kr[sl]);
+                            sA = mfma16(w, qa[16 + u], sA);
+                            sB = mfma16(w, qb[16 + u], sB);
                         } else {
-                            const int grp = (u - 2) >> 1, pr = (u - 2) & 1;
-                            if (pr == 0) { p0 = f32x4{0.f, 0.f, 0.f, 0.f}; p1 = p0; }
-                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][0], ka[sl][1]), qreg[4 * grp + 2 * pr], p0);
-                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][0], kb[sl][1]), qreg[4 * grp + 2 * pr], p1);
-                            p0 = mfma16(e4m3x8_to_bf16(ka[sl][2], ka[sl][3]), qreg[4 * grp + 2 * pr + 1], p0);
-                            p1 = mfma16(e4m3x8_to_bf16(kb[sl][2], kb[sl][3]), qreg[4 * grp + 2 * pr + 1], p1);
-                            if (pr == 1) {
+                            const int grp = (u - 2) >> 1, pq = (u - 2) & 1;
+                            if (pq == 0) { pA = f32x4{0.f, 0.f, 0.f, 0.f}; pB = pA; }
+                            const bf16x8 w0 = e4m3x8_to_bf16(kr[sl][0], kr[sl][1]);
+                            const bf16x8 w1 = e4m3x8_to_bf16(kr[sl][2], kr[sl][3]);
+                            pA = mfma16(w0, qa[4 * grp + 2 * pq], pA);
+                            pB = mfma16(w0, qb[4 * grp + 2 * pq], pB);
+                            pA = mfma16(w1, qa[4 * grp + 2 * pq + 1], pA);
+                            pB = mfma16(w1, qb[4 * grp + 2 * pq + 1], pB);
+                            if (pq == 1) {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    s0[e] += sc0[e][grp] * p0[e];
-                                    s1[e] += sc1[e][grp] * p1[e];
+                                    sA[e] += sc[e][grp] * pA[e];
+                                    sB[e] += sc[e][grp] * pB[e];
                                 }
                             }
                         }
-                        if (u + PF < 10) {
-                            ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
-                            kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
-                        }
+                        if (u + PF < 10) kr[sl] = lds_load<u32x4>(st + unit_off(u + PF));
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF + 8, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, PF + 4, 0);
 #pragma unroll
                     for (int u = 0; u < 10 - PF; ++u) {
                         if (u < 2)
                             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                         else
                             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, 4 * PF, 0);
-                }
+                    }
 
-                // ---- mask, reference, softmax weights (base 2)
-                float sv[8];
+                    // ---- mask, reference, softmax weights (base 2)
+                    float sv[8];  // [0..3]: headA, tokens tokC + e; [4..7]: headB
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sv[e] = v0[e] >= 0 ? s0[e] * a.scale_log2 : -INFINITY;
-                    sv[4 + e] = v1[e] >= 0 ? s1[e] * a.scale_log2 : -INFINITY;
-                }
-                float mx = sv[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-                if (!ref_set) {
-                    // first tile with a valid token (the same tile for every head and wave)
-                    const bool any_valid = v0[0] >= 0 || v0[1] >= 0 || v0[2] >= 0 || v0[3] >= 0 || v1[0] >= 0 ||
-                                           v1[1] >= 0 || v1[2] >= 0 || v1[3] >= 0;
-                    if (__any(any_valid)) {
-                        mx = fmaxf(mx, __shfl_xor(mx, 16));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32));
-                        m_ref = mx;
-                        ref_set = true;
+                    for (int e = 0; e < 4; ++e) {
+                        sv[e] = vc[e] >= 0 ? sA[e] * a.scale_log2 : -INFINITY;
+                        sv[4 + e] = vc[e] >= 0 ? sB[e] * a.scale_log2 : -INFINITY;
                     }
-                } else if (__any(mx > m_ref + kMaxRise)) {  // rare: raise the references of this wave's heads
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    const bool up = mx > m_ref + kMaxRise;
-                    const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
-                    m_ref = up ? mx : m_ref;
-                    l_run *= alpha;
-                    if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_ALPHA + (k & 1) * (kHeads * 4) + 4 * head) = alpha;
-                    raised = 1;
-                }
-                const float m_use = ref_set ? m_ref : 0.f;
-                // The denominator sums the fp32 weights; the PV product takes them
-                // rounded to bf16 once (for fp8 rows after multiplying by the
-                // token's scale of each 128-group, one copy per group).
-                float pf[8];
-                float psum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pf[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-                    psum += pf[e];
-                }
-                l_run += psum;
-                lds_u8* const pbuf = p_mine + (k & 1) * PBUF;
-                if (FMT == 0) {
-                    bf16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pf[e];
-                    *(__attribute__((address_space(3))) bf16x8*)pbuf = pb;
-                } else if (FMT == 2) {
-                    // copies 0..6: the weights times each token's scale of nope group c;
-                    // copy 7 (rope values): the weights
-                    const lds_u8* rec = lds + (k % NST) * STAGE + REC_OFF;
-                    const i32x4 c0a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0);
-                    const i32x4 c0b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0 + 16);
-                    const i32x4 c1a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1);
-                    const i32x4 c1b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1 + 16);
-                    const i32x2 rc[8] = {i32x2{c0a[0], c0a[1]}, i32x2{c0a[2], c0a[3]}, i32x2{c0b[0], c0b[1]},
-                                         i32x2{c0b[2], c0b[3]}, i32x2{c1a[0], c1a[1]}, i32x2{c1a[2], c1a[3]},
-                                         i32x2{c1b[0], c1b[1]}, i32x2{c1b[2], c1b[3]}};
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        bf16x8 pg;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) pg[e] = (__bf16)(c < 7 ? pf[e] * ue8m0_scale(rc[e], c) : pf[e]);
-                        *(__attribute__((address_space(3))) bf16x8*)(pbuf + c * kPBytesPerCopy) = pg;
-                    }
-                } else {
-#pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        bf16x8 pg;
+                    float mA = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                    float mB = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
+                    mA = head_max(mA);
+                    mB = head_max(mB);
+                    swap_post(mA, mB, k + 2);
+                    // The weights against the references, and their P copies.  The
+                    // denominator sums the fp32 weights; the PV product takes them
+                    // rounded to bf16 once (for fp8 rows after multiplying by the
+                    // token's scale of each 128-group, one copy per group).
+                    float psA = 0.f, psB = 0.f;
+                    lds_u8* const pbuf = p_mine + (k & 1) * PBUF;  // headA; headB at + pb_off
+                    auto weights = [&](float muA, float muB) {
+                        float pf[8];
+                        psA = 0.f;
+                        psB = 0.f;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            pg[e] = (__bf16)(pf[e] * sc0[e][grp]);
-                            pg[4 + e] = (__bf16)(pf[4 + e] * sc1[e][grp]);
+                            pf[e] = __builtin_amdgcn_exp2f(sv[e] - muA);
+                            pf[4 + e] = __builtin_amdgcn_exp2f(sv[4 + e] - muB);
+                            psA += pf[e];
+                            psB += pf[4 + e];
                         }
-                        *(__attribute__((address_space(3))) bf16x8*)(pbuf + grp * kPBytesPerCopy) = pg;
+                        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+#pragma unroll
+                            for (int grp = 0; grp < 4; ++grp) {
+                                bf16x4 wa, wb;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    wa[e] = (__bf16)(pf[e] * sc[e][grp]);
+                                    wb[e] = (__bf16)(pf[4 + e] * sc[e][grp]);
+                                }
+                                *(lds_bf16x4*)(pbuf + grp * kPBytesPerCopy) = wa;
+                                *(lds_bf16x4*)(pbuf + grp * kPBytesPerCopy + pb_off) = wb;
+                            }
+                    };
+                    // Once the references are set, the weights are taken against them
+                    // while the partner's maxima are on their way; they are redone in
+                    // the rare step that raises a reference (the PV waves read P only
+                    // after the step's barrier).  Until then, the first tile with a
+                    // valid token sets the references from both halves' maxima.
+                    if (ref_set) weights(mrA, mrB);
+                    {
+                        float oA, oB;
+                        swap_wait(k + 2, oA, oB);
+                        mA = fmaxf(mA, oA);  // the tile's maximum of headA over both halves
+                        mB = fmaxf(mB, oB);
+                    }
+                    bool redo = false;
+                    if (!ref_set) {
+                        // first tile with a valid token (the same tile for every head and wave)
+                        const bool any_valid = vc[0] >= 0 || vc[1] >= 0 || vc[2] >= 0 || vc[3] >= 0 || vo[0] >= 0 ||
+                                               vo[1] >= 0 || vo[2] >= 0 || vo[3] >= 0;
+                        if (__any(any_valid)) {
+                            mrA = mA;
+                            mrB = mB;
+                            ref_set = true;
+                        }
+                        redo = true;
+                    } else if (__any(mA > mrA + kMaxRise || mB > mrB + kMaxRise)) {  // rare: raise the references
+                        const bool upA = mA > mrA + kMaxRise, upB = mB > mrB + kMaxRise;
+                        const float alA = upA ? __builtin_amdgcn_exp2f(mrA - mA) : 1.f;
+                        const float alB = upB ? __builtin_amdgcn_exp2f(mrB - mB) : 1.f;
+                        mrA = upA ? mA : mrA;
+                        mrB = upB ? mB : mrB;
+                        lA *= alA;
+                        lB *= alB;
+                        if (half == 0 && g == 0) {
+                            __attribute__((address_space(3))) float* al =
+                                (__attribute__((address_space(3))) float*)(aux + AUX_ALPHA + (k & 1) * (kHeads * 4));
+                            al[headA] = alA;
+                            al[headB] = alB;
+                        }
+                        raised = 1;
+                        redo = true;
+                    }
+                    if (redo) weights(ref_set ? mrA : 0.f, ref_set ? mrB : 0.f);
+                    lA += psA;
+                    lB += psB;
+                }
+                if (half == 0 && lane == 0)
+                    *(__attribute__((address_space(3))) i32x2*)(aux + AUX_FLAG + 16 * (k & 1) + 8 * hp) = i32x2{raised, raised};
+                if (k == ntiles) {
+                    // ---- denominators and lse of headA and headB: final since step
+                    // ntiles - 1, published in the last step (the PV waves still add
+                    // the last tile), so the barrier that ends it makes them visible
+                    float tA = head_sum(lA), tB = head_sum(lB);
+                    float oA, oB;
+                    swap_post(tA, tB, ntiles + 2);
+                    swap_wait(ntiles + 2, oA, oB);
+                    if (half == 0 && g == 0) {
+                        tA += oA;
+                        tB += oB;
+                        __attribute__((address_space(3))) float* dn = (__attribute__((address_space(3))) float*)(aux + AUX_DENOM);
+                        dn[headA] = ref_set ? tA : 0.f;
+                        dn[headB] = ref_set ? tB : 0.f;
+                        lbase[headA] = ref_set ? (mrA + log2f(tA)) * kLn2 : -INFINITY;
+                        lbase[headB] = ref_set ? (mrB + log2f(tB)) * kLn2 : -INFINITY;
                     }
                 }
+                if (LPT_QK > 0 && k + 1 < ntiles) wait_tiles<LPT_QK>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
+                __syncthreads();  // E_k
             }
-            if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 16 * (k & 1) + 4 * q) = raised;
-            if (k == ntiles) {
-                // ---- denominator and lse of `head`: final since step ntiles - 1,
-                // published in the last step (the PV waves still add the last
-                // tile), so the barrier that ends it makes them visible
-                float l_tot = l_run;
-                l_tot += __shfl_xor(l_tot, 16);
-                l_tot += __shfl_xor(l_tot, 32);
-                if (g == 0) {
-                    *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
-                    const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-                    lbase[head] = lse_v;
+
+            __syncthreads();  // the PV waves have staged every head
+            store_all();
+        } else {
+            // =================== QK waves: heads [16q, 16q + 16) ===================
+            const int q = wave;
+            const int head = 16 * q + i16;
+            // Q of `head` as the B operand of S^T = K . Q^T (8 dims of k-step kk per
+            // lane).  (v4 rows: the 16-byte run of nope group u feeds k-steps 2u
+            // and 2u+1; k-steps 14 and 15 are the rope values.)
+            constexpr int NQ = FMT == 2 ? 16 : 18;
+            bf16x8 qreg[NQ];
+            {
+                const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * DQK;
+#pragma unroll
+                for (int kk = 0; kk < NQ; ++kk) {
+                    const int d = FMT == 0  ? 32 * kk + 8 * g
+                                  : kk < 14 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1)
+                                            : kNopeV4 + 32 * (kk - 14) + 8 * g;
+                    qreg[kk] = *(const bf16x8*)(qh + d);
                 }
             }
-            if (LPT_QK > 0 && k + 1 < ntiles) wait_tiles<LPT_QK>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
-            __syncthreads();  // E_k
-        }
+            __syncthreads();  // T1
+            __syncthreads();  // B0
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
 
-        __syncthreads();  // the PV waves have staged every head
-        store_all();
+            // K operand rows of the two 16-token blocks: tokens i16 and 16 + i16.
+            // Accumulator entry e of a lane: tokens 4g + e (block 0), 16 + 4g + e (block 1).
+            const int tokA0 = i16, tokA1 = 16 + i16;
+            const int tokC0 = 4 * g, tokC1 = 16 + 4 * g;
+            int qk0[2], qk1[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                qk0[e] = tokA0 * 128 + (((4 * e + g) ^ swz(tokA0)) << 4);
+                qk1[e] = tokA1 * 128 + (((4 * e + g) ^ swz(tokA1)) << 4);
+            }
+            // v4: this lane's chunk of the half band (rope values 32 + 8g .. 32 + 8g + 7)
+            const int qh0 = HALF_OFF + tokA0 * 64 + ((g ^ swz4(tokA0)) << 4);
+            const int qh1 = HALF_OFF + tokA1 * 64 + ((g ^ swz4(tokA1)) << 4);
+            // P slot of this lane: (block q, group g, lane i16): its 8 weights are
+            // the k-slots 8g .. 8g + 7 of the PV B operand, i.e. tokens
+            // 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3.
+            lds_u8* const p_mine = aux + ((q * 4 + g) * 16 + i16) * 16;  // + buffer (+ group copy for fp8)
+
+            // Online softmax of `head`, base 2.  Weights are taken against a
+            // reference maximum m_ref, set at the first tile with a valid token;
+            // it is raised only when a tile's maximum exceeds it by more than
+            // kMaxRise (weights up to 2^kMaxRise stay finite in fp32 and bf16), and
+            // then the denominator here and the output accumulators of the PV waves
+            // are rescaled by alpha = 2^(old - new).
+            constexpr float kMaxRise = 32.f;
+            float m_ref = -INFINITY;  // the same in the four lanes of the head
+            float l_run = 0.f;        // this lane's share of the denominator
+            bool ref_set = false;     // the same in every lane of the wave
+            const int pro = min(NST - 1, ntiles);  // tiles issued before the loop
+            if (LPT_QK > 0) {
+                for (int t = 0; t < pro; ++t) {
+                    const Gather gt = prepare(t);
+#pragma unroll
+                    for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+                }
+                if (ntiles > 0) wait_tiles<LPT_QK>(pro - 1);  // this wave's part of tile 0 has landed
+            }
+            __syncthreads();  // P0
+            for (int k = 0; k <= ntiles; ++k) {
+                int raised = 0;
+                // tile k + NST - 1 goes into the stage of tile k - 1 (free since E_{k-1})
+                if (LPT_QK > 0 && k + NST - 1 < ntiles) {
+                    const Gather gt = prepare(k + NST - 1);
+#pragma unroll
+                    for (int i = 0; i < LPT_QK; ++i) issue_one(gt, i);
+                }
+                if (k < ntiles) {
+                    const lds_u8* st = lds + (k % NST) * STAGE;
+                    const lds_u8* rt = rowtab + 4 * k * kTile;
+                    const i32x4 v0 = lds_load<i32x4>(rt + 4 * tokC0);
+                    const i32x4 v1 = lds_load<i32x4>(rt + 4 * tokC1);
+
+                    // ---- S^T = K . Q^T for the tile's 32 tokens, in two 16-token blocks
+                    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+                    if (FMT == 0) {
+                        constexpr int PF = 4;  // k-steps of K operands in flight
+                        bf16x8 ka[PF], kb[PF];
+#pragma unroll
+                        for (int kk = 0; kk < PF; ++kk) {
+                            ka[kk] = lds_load<bf16x8>(st + qk0[kk & 1] + (kk >> 1) * kTile * 128);
+                            kb[kk] = lds_load<bf16x8>(st + qk1[kk & 1] + (kk >> 1) * kTile * 128);
+                        }
+#pragma unroll
+                        for (int kk = 0; kk < 18; ++kk) {
+                            const int sl = kk % PF;
+                            s0 = mfma16(ka[sl], qreg[kk], s0);
+                            s1 = mfma16(kb[sl], qreg[kk], s1);
+                            if (kk + PF < 18) {
+                                const int kn = kk + PF;
+                                ka[sl] = lds_load<bf16x8>(st + qk0[kn & 1] + (kn >> 1) * kTile * 128);
+                                kb[sl] = lds_load<bf16x8>(st + qk1[kn & 1] + (kn >> 1) * kTile * 128);
+                            }
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+                        for (int i = 0; i < 18 - PF; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+                    } else {
+                        // 9 load units per block: nope groups 0..6 (16 e4m3 values of this
+                        // lane's token, two k-steps, widened with the token's scale of
+                        // that group), then rope values 0..31 and 32..63 (bf16)
+                        constexpr int PF = 3;
+                        u32x4 ka[PF], kb[PF];
+                        auto unit_off = [&](int u, int blk) {
+                            const int* qo = blk == 0 ? qk0 : qk1;
+                            return u < 8 ? qo[u & 1] + (u >> 1) * kTile * 128 : (blk == 0 ? qh0 : qh1);
+                        };
+#pragma unroll
+                        for (int u = 0; u < PF; ++u) {
+                            ka[u] = lds_load<u32x4>(st + unit_off(u, 0));
+                            kb[u] = lds_load<u32x4>(st + unit_off(u, 1));
+                        }
+                        const i32x2 ra = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA0);
+                        const i32x2 rb = lds_load<i32x2>(st + REC_OFF + kScaleRecBytesV4 * tokA1);
+#pragma unroll
+                        for (int u = 0; u < 9; ++u) {
+                            const int sl = u % PF;
+                            if (u < 7) {
+                                const float fa = ue8m0_scale(ra, u), fb = ue8m0_scale(rb, u);
+                                s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][0], ka[sl][1], fa), qreg[2 * u], s0);
+                                s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][0], kb[sl][1], fb), qreg[2 * u], s1);
+                                s0 = mfma16(e4m3x8_scaled_to_bf16(ka[sl][2], ka[sl][3], fa), qreg[2 * u + 1], s0);
+                                s1 = mfma16(e4m3x8_scaled_to_bf16(kb[sl][2], kb[sl][3], fb), qreg[2 * u + 1], s1);
+                            } else {
+                                s0 = mfma16(__builtin_bit_cast(bf16x8, ka[sl]), qreg[7 + u], s0);
+                                s1 = mfma16(__builtin_bit_cast(bf16x8, kb[sl]), qreg[7 + u], s1);
+                            }
+                            if (u + PF < 9) {
+                                ka[sl] = lds_load<u32x4>(st + unit_off(u + PF, 0));
+                                kb[sl] = lds_load<u32x4>(st + unit_off(u + PF, 1));
+                            }
+                        }
+                    }
+
+                    // ---- mask, reference, softmax weights (base 2)
+                    float sv[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sv[e] = v0[e] >= 0 ? s0[e] * a.scale_log2 : -INFINITY;
+                        sv[4 + e] = v1[e] >= 0 ? s1[e] * a.scale_log2 : -INFINITY;
+                    }
+                    float mx = sv[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+                    if (!ref_set) {
+                        // first tile with a valid token (the same tile for every head and wave)
+                        const bool any_valid = v0[0] >= 0 || v0[1] >= 0 || v0[2] >= 0 || v0[3] >= 0 || v1[0] >= 0 ||
+                                               v1[1] >= 0 || v1[2] >= 0 || v1[3] >= 0;
+                        if (__any(any_valid)) {
+                            mx = fmaxf(mx, __shfl_xor(mx, 16));
+                            mx = fmaxf(mx, __shfl_xor(mx, 32));
+                            m_ref = mx;
+                            ref_set = true;
+                        }
+                    } else if (__any(mx > m_ref + kMaxRise)) {  // rare: raise the references of this wave's heads
+                        mx = fmaxf(mx, __shfl_xor(mx, 16));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32));
+                        const bool up = mx > m_ref + kMaxRise;
+                        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+                        m_ref = up ? mx : m_ref;
+                        l_run *= alpha;
+                        if (g == 0) *(__attribute__((address_space(3))) float*)(aux + AUX_ALPHA + (k & 1) * (kHeads * 4) + 4 * head) = alpha;
+                        raised = 1;
+                    }
+                    const float m_use = ref_set ? m_ref : 0.f;
+                    // The denominator sums the fp32 weights; the PV product takes them
+                    // rounded to bf16 once (for v4 rows after multiplying by the
+                    // token's scale of each 64-group, one copy per group).
+                    float pf[8];
+                    float psum = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pf[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+                        psum += pf[e];
+                    }
+                    l_run += psum;
+                    lds_u8* const pbuf = p_mine + (k & 1) * PBUF;
+                    if (FMT == 0) {
+                        bf16x8 pb;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pf[e];
+                        *(__attribute__((address_space(3))) bf16x8*)pbuf = pb;
+                    } else {
+                        // copies 0..6: the weights times each token's scale of nope group c;
+                        // copy 7 (rope values): the weights
+                        const lds_u8* rec = lds + (k % NST) * STAGE + REC_OFF;
+                        const i32x4 c0a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0);
+                        const i32x4 c0b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC0 + 16);
+                        const i32x4 c1a = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1);
+                        const i32x4 c1b = lds_load<i32x4>(rec + kScaleRecBytesV4 * tokC1 + 16);
+                        const i32x2 rc[8] = {i32x2{c0a[0], c0a[1]}, i32x2{c0a[2], c0a[3]}, i32x2{c0b[0], c0b[1]},
+                                             i32x2{c0b[2], c0b[3]}, i32x2{c1a[0], c1a[1]}, i32x2{c1a[2], c1a[3]},
+                                             i32x2{c1b[0], c1b[1]}, i32x2{c1b[2], c1b[3]}};
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            bf16x8 pg;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) pg[e] = (__bf16)(c < 7 ? pf[e] * ue8m0_scale(rc[e], c) : pf[e]);
+                            *(__attribute__((address_space(3))) bf16x8*)(pbuf + c * kPBytesPerCopy) = pg;
+                        }
+                    }
+                }
+                if (lane == 0) *(__attribute__((address_space(3))) int*)(aux + AUX_FLAG + 16 * (k & 1) + 4 * q) = raised;
+                if (k == ntiles) {
+                    // ---- denominator and lse of `head`: final since step ntiles - 1,
+                    // published in the last step (the PV waves still add the last
+                    // tile), so the barrier that ends it makes them visible
+                    float l_tot = l_run;
+                    l_tot += __shfl_xor(l_tot, 16);
+                    l_tot += __shfl_xor(l_tot, 32);
+                    if (g == 0) {
+                        *(__attribute__((address_space(3))) float*)(aux + AUX_DENOM + 4 * head) = ref_set ? l_tot : 0.f;
+                        const float lse_v = ref_set ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+                        lbase[head] = lse_v;
+                    }
+                }
+                if (LPT_QK > 0 && k + 1 < ntiles) wait_tiles<LPT_QK>(min(NST - 2, ntiles - 2 - k));  // its part of tile k+1 has landed
+                __syncthreads();  // E_k
+            }
+
+            __syncthreads();  // the PV waves have staged every head
+            store_all();
+        }
     } else {
         // ========= PV waves: value dims [128p, 128p + 128), all heads =========
         const int p = wave - 4;

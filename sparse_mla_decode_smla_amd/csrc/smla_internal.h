@@ -68,15 +68,19 @@ constexpr int kStagesV4 = 4;
 //          the rope values (8 copies);
 //   alpha  per-head factors [64] fp32 that rescale the output accumulators
 //          when a head's reference maximum was raised at that tile;
-//   flags  one int per QK wave: it raised a reference at that tile;
-// then denom, the per-head softmax denominators [64] fp32.
+//   flags  one int per 16-head block: its references were raised at that tile;
+// then denom, the per-head softmax denominators [64] fp32, and (fp8 rows)
+// the area in which the two QK waves that share 32 heads swap per-head
+// values once a step: per QK wave, 16 records of 16 bytes (two heads' values
+// and a step tag twice).
 constexpr int kPBytesPerCopy = kHeads * kTile * 2;
 inline constexpr int aux_p_copies(int kv_format) { return kv_format == 0 ? 1 : kv_format == 1 ? 4 : 8; }
 inline constexpr int aux_p_buffer_bytes(int kv_format) { return aux_p_copies(kv_format) * kPBytesPerCopy; }
 inline constexpr int aux_alpha_offset(int kv_format) { return 2 * aux_p_buffer_bytes(kv_format); }
 inline constexpr int aux_flag_offset(int kv_format) { return aux_alpha_offset(kv_format) + 2 * kHeads * 4; }
 inline constexpr int aux_denom_offset(int kv_format) { return aux_flag_offset(kv_format) + 2 * 16; }
-inline constexpr int aux_bytes(int kv_format) { return aux_denom_offset(kv_format) + kHeads * 4; }
+inline constexpr int aux_swap_offset(int kv_format) { return aux_denom_offset(kv_format) + kHeads * 4; }
+inline constexpr int aux_bytes(int kv_format) { return aux_swap_offset(kv_format) + (kv_format == 1 ? 4 * 16 * 16 : 0); }
 
 constexpr int kLdsLimit = 160 * 1024;  // bytes of LDS a gfx950 workgroup may use
 
