@@ -200,16 +200,19 @@ def test_query_magnitudes(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS[:2], ids=FMT_IDS[:2])
-def test_late_large_scores_restart(fmt):
+@pytest.mark.parametrize("pos", [230, 250], ids=["tokens0-15", "tokens16-31"])
+def test_late_large_scores_restart(fmt, pos):
     # A token near the end of each list gets a score far above the first tiles' max
     # (the rope part of its K row is a large multiple of head 0's rope query; its V
     # part stays as generated), so the kernel must raise its softmax reference after
-    # accumulating; forced splits keep several tiles per part.
+    # accumulating; forced splits keep several tiles per part.  The token sits in
+    # the first or the second half of its tile (list position 230 or 250: for fp8
+    # rows the two halves belong to different QK waves, which must raise together).
     inp = I.small_inputs(batch=2, q_len=1, topk=256, seq_len=512, kv_format=fmt, seed=90)
     w = inp.workload
     kv = inp.kv_cache.reshape(-1, w.row_bytes).copy()
     for b in range(2):
-        p = int(inp.indices[b, 0, 250])
+        p = int(inp.indices[b, 0, pos])
         row = int(inp.block_table[b, p // 64]) * 64 + p % 64
         qf = (inp.q[b, 0, 0].astype(np.uint32) << 16).view(np.float32)
         kf = oracle_pins.token_rows(inp, b, np.array([p]))[0].astype(np.float32)
@@ -222,6 +225,30 @@ def test_late_large_scores_restart(fmt):
     for splits in (1, 2):
         out, lse = run_gpu(inp2, force_splits=splits)
         check(out, lse, ref_o, ref_l, f"late large score S{splits}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+def test_first_valid_token_in_one_half_of_a_tile(fmt):
+    """The softmax reference is set at the first tile with a valid token.  For fp8 rows the two
+    halves of a tile (tokens 0-15, 16-31) belong to two QK waves that must set it together: rows
+    whose first valid tokens all lie in one half of a tile, or in one token of a later tile."""
+    inp = I.small_inputs(batch=4, q_len=1, topk=128, seq_len=600, kv_format=fmt, seed=160 + fmt)
+    idx = inp.indices.copy()
+    idx[0, 0, 0:16] = -1          # tile 0: only tokens 16..31 valid
+    idx[1, 0, 16:32] = -1         # tile 0: only tokens 0..15 valid
+    idx[2, 0, 0:52] = -1          # tiles 0, 1 masked but token 52 (tile 1, second half) ...
+    idx[2, 0, 53:64] = -1         # ... alone in tile 1
+    idx[3, 0, 0:32] = -1          # tile 0 masked, tile 1 only token 33 (first half)
+    idx[3, 0, 34:64] = -1
+    idx[3, 0, 32] = -1
+    ref_o, ref_l = oracle.default().sparse_mla_decode(inp.q, inp.kv_cache, inp.block_table, idx, inp.seq_lens,
+                                                      inp.softmax_scale, d_v=inp.workload.d_v, kv_format=fmt,
+                                                      block_size=64, threads=8)
+    assert np.isfinite(ref_l).all()
+    for splits in (1, 2):
+        note(f"first valid token in one half fmt={fmt} S={splits}")
+        out, lse = run_gpu(inp, indices=idx, force_splits=splits)
+        check(out, lse, ref_o, ref_l, f"one-half first tile fmt{fmt} S{splits}")
 
 
 def test_late_large_scores_v4():
