@@ -252,7 +252,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ntiles = (nk + kTile - 1) / kTile;
 
     // ---- logical positions -> physical rows (masked entries -> -1), by the PV
-    // waves (threads 256..511) while the QK waves load Q.  The index list
+    // waves (threads 256..511); the QK waves load Q only once the copies below
+    // have landed (T1): Q's first-touch loads issued next to them had held the
+    // copies up by about half a microsecond.  The index list
     // goes into the row table, and (when the sequence's block-table row is
     // short) the block-table row into the still empty stage ring, by LDS-DMA:
     // every copy instruction is issued before the one wait, so the copy costs
@@ -481,21 +483,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // k-step kk per lane); for fp8 rows the c_kv dims of k-steps 2p and
             // 2p+1 inside a 128-group are the two halves of one 16-byte run, so
             // one LDS read feeds two k-steps.
-            // Each wave loads block A from HBM before T1, as every QK wave loads
-            // one block, and hands it to its partner through the stages of tiles
-            // 2 .. (and the P buffers), which are empty until P0: loading both
+            // Each wave loads block A from HBM between T1 and B0, as every QK wave
+            // loads one block, and hands it to its partner through the stages of
+            // tiles 2 .. (and the P buffers), which are empty until P0: loading both
             // blocks from HBM made the first-touch loads of the second block (whose
             // address translations miss) hold up the first tiles' gathers.
             constexpr int NQ = 18;
             bf16x8 qa[NQ], qb[NQ];
-            {
-                const uint16_t* const qh = a.q + ((int64_t)r * kHeads + headA) * DQK;
-#pragma unroll
-                for (int kk = 0; kk < NQ; ++kk) {
-                    const int d = kk >= 16 ? 32 * kk + 8 * g : 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
-                    qa[kk] = *(const bf16x8*)(qh + d);
-                }
-            }
             // this wave's slot in the swap area: 16-byte records {headA, headB, seq, seq}
             // per head of a block (read by the partner only after T1)
             typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
@@ -547,6 +541,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 return u + v;
             };
             __syncthreads();  // T1
+            {
+                const uint16_t* const qh = a.q + ((int64_t)r * kHeads + headA) * DQK;
+#pragma unroll
+                for (int kk = 0; kk < NQ; ++kk) {
+                    const int d = kk >= 16 ? 32 * kk + 8 * g : 128 * (kk >> 2) + 64 * ((kk >> 1) & 1) + 16 * g + 8 * (kk & 1);
+                    qa[kk] = *(const bf16x8*)(qh + d);
+                }
+            }
             __syncthreads();  // B0
             wait_vmcnt<0>();
             static_assert(2 * STAGE + 4 * NQ * 1024 <= NST * STAGE + 2 * PBUF && NST >= 3,
@@ -793,6 +795,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // and 2u+1; k-steps 14 and 15 are the rope values.)
             constexpr int NQ = FMT == 2 ? 16 : 18;
             bf16x8 qreg[NQ];
+            __syncthreads();  // T1 (Q is loaded after it: see the row table)
             {
                 const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * DQK;
 #pragma unroll
@@ -803,7 +806,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     qreg[kk] = *(const bf16x8*)(qh + d);
                 }
             }
-            __syncthreads();  // T1
             __syncthreads();  // B0
             wait_vmcnt<0>();
 #pragma unroll
