@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ntiles = (nk + kTile - 1) / kTile;
 
     // ---- logical positions -> physical rows (masked entries -> -1), by the PV
-    // waves (threads 256..511); the QK waves load Q only once the copies below
+    // waves (threads 256..511); the QK waves copy Q only once the copies below
     // have landed (T1): Q's first-touch loads issued next to them had held the
     // copies up by about half a microsecond.  The index list
     // goes into the row table, and (when the sequence's block-table row is
@@ -466,6 +466,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // refilling the stage of tile k-1 with tile k + NST - 1, copy their V slice
     // of tile k into registers and wait for tile k+1 to land.  NST - 2 tiles
     // beyond the next one are in flight while a tile is computed.
+    // ---- query staging: a QK wave's 16 query rows (HB bytes each, contiguous in
+    // HBM) are copied into LDS by LDS-DMA, 1 KB per instruction, with the 16-byte
+    // chunks of each row XOR-swizzled so that the operand reads (16 rows, the
+    // same chunk) fall on distinct banks: bf16 rows (1152 bytes) keep groups of 8
+    // chunks and swizzle by row / 2 (odd rows start 128 bytes further into the
+    // banks), v4 rows (1024 bytes) swizzle groups of 16 chunks by row.
+    constexpr int HB = DQK * 2;
+    auto q_swz = [](int h, int c) {
+        return FMT == 2 ? (c & ~15) | ((c ^ h) & 15) : (c & ~7) | ((c ^ (h >> 1)) & 7);
+    };
+    // copy 16 rows starting at row `row0` of this workgroup's query into LDS at `dst`
+    auto q_copy = [&](int row0, unsigned dst) {
+        const unsigned char* qsrc = (const unsigned char*)(a.q + ((int64_t)r * kHeads + row0) * DQK);
+#pragma unroll
+        for (int j = 0; j < 16 * HB / 1024; ++j) {
+            const int o = j * 1024 + 16 * lane;
+            const int h = o / HB;
+            lds_dma16<false>(qsrc + h * HB + 16 * q_swz(h, (o - h * HB) / 16), dst + j * 1024);
+        }
+    };
+    // operand of row i16, dims d .. d + 7, from a staged block at `src`
+    auto q_read = [&](const lds_u8* src, int d) { return lds_load<bf16x8>(src + i16 * HB + 16 * q_swz(i16, d / 8)); };
     if (wave < 4) {
         if constexpr (FMT == 1) {
             // ====== QK waves: wave 2c + h, heads [32c, 32c + 32), tokens [16h, 16h + 16) of each tile ======
@@ -483,11 +505,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // k-step kk per lane); for fp8 rows the c_kv dims of k-steps 2p and
             // 2p+1 inside a 128-group are the two halves of one 16-byte run, so
             // one LDS read feeds two k-steps.
-            // Each wave loads block A from HBM between T1 and B0, as every QK wave
-            // loads one block, and hands it to its partner through the stages of
-            // tiles 2 .. (and the P buffers), which are empty until P0: loading both
-            // blocks from HBM made the first-touch loads of the second block (whose
-            // address translations miss) hold up the first tiles' gathers.
+            // Each wave loads block A from HBM between T1 and B0 (see the row
+            // table), as every QK wave loads one block, and hands it to its
+            // partner through the stages of tiles 2 .. (and the P buffers), which
+            // are empty until P0: loading both blocks from HBM made the first-touch
+            // loads of the second block (whose address translations miss) hold up
+            // the first tiles' gathers.  (Staging the block by LDS-DMA, as the other
+            // layouts do, measured 0.3-0.8 us slower here.)
             constexpr int NQ = 18;
             bf16x8 qa[NQ], qb[NQ];
             // this wave's slot in the swap area: 16-byte records {headA, headB, seq, seq}
@@ -540,6 +564,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 lane_swap16(u, v);
                 return u + v;
             };
+            static_assert(2 * STAGE + 4 * NQ * 1024 <= NST * STAGE + 2 * PBUF && NST >= 3,
+                          "the query hand-over area exceeds the stages of tiles 2.. and the P buffers");
             __syncthreads();  // T1
             {
                 const uint16_t* const qh = a.q + ((int64_t)r * kHeads + headA) * DQK;
@@ -551,8 +577,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             __syncthreads();  // B0
             wait_vmcnt<0>();
-            static_assert(2 * STAGE + 4 * NQ * 1024 <= NST * STAGE + 2 * PBUF && NST >= 3,
-                          "the query hand-over area exceeds the stages of tiles 2.. and the P buffers");
             {
                 // ---- the query hand-over: this wave's block A is the partner's block
                 // B.  (The hand-over and the swaps share the records: tag 1 here,
@@ -795,19 +819,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // and 2u+1; k-steps 14 and 15 are the rope values.)
             constexpr int NQ = FMT == 2 ? 16 : 18;
             bf16x8 qreg[NQ];
-            __syncthreads();  // T1 (Q is loaded after it: see the row table)
+            // The wave's 16 query rows are staged in LDS (`q_copy`) between T1 and
+            // B0 (see the row table) and read from there in operand order after B0.
+            // They go to the stages of tiles 2 .. (and the P buffers), which are
+            // empty until P0.  (Loading the operands directly, 16 rows 1152 bytes
+            // apart in every instruction, took about a microsecond to issue and held
+            // B0 up.)
+            static_assert(2 * STAGE + 4 * NQ * 1024 <= NST * STAGE + 2 * PBUF && NST >= 3,
+                          "the query staging area exceeds the stages of tiles 2.. and the P buffers");
+            __syncthreads();  // T1
+            q_copy(16 * q, lds0 + (unsigned)(2 * STAGE + q * NQ * 1024));
+            __syncthreads();  // B0
+            wait_vmcnt<0>();
             {
-                const uint16_t* qh = a.q + ((int64_t)r * kHeads + head) * DQK;
+                const lds_u8* xq = lds + 2 * STAGE + q * NQ * 1024;
 #pragma unroll
                 for (int kk = 0; kk < NQ; ++kk) {
                     const int d = FMT == 0  ? 32 * kk + 8 * g
                                   : kk < 14 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1)
                                             : kNopeV4 + 32 * (kk - 14) + 8 * g;
-                    qreg[kk] = *(const bf16x8*)(qh + d);
+                    qreg[kk] = q_read(xq, d);
                 }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before P0 (tile 2 is gathered there after it)
             }
-            __syncthreads();  // B0
-            wait_vmcnt<0>();
 #pragma unroll
             for (int kk = 0; kk < NQ; ++kk) asm volatile("" : "+v"(qreg[kk]));  // loads done; no waits in the loop
 
