@@ -86,7 +86,14 @@ __global__ __launch_bounds__(64 * NW) void combine_kernel(const uint16_t* __rest
                                                           int64_t pairs, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
     __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][2][64];
-    const int64_t pair = blockIdx.x;
+    // (row, head) pairs are dealt to workgroup ids as the partial kernel deals
+    // its (row, part) items: consecutive ids go round-robin over the 8 XCDs, and
+    // the pairs of XCD x are the x-th eighth of all pairs, so a row's pairs run
+    // on the XCD (and read from the L2) where the partial kernel wrote that
+    // row's parts whenever the rows divide evenly over the XCDs.  (A bijection
+    // of [0, pairs).)
+    const int64_t xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int64_t pair = xcd * (pairs >> 3) + min(xcd, pairs & 7) + within;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
