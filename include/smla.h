@@ -89,9 +89,10 @@ typedef enum {
  * combine kernel of smla_decode_run then reads with non-temporal loads.  The
  * arithmetic, and so every result, is the same under every policy.
  * SMLA_CACHE_AUTO lets the plan choose from the problem shape: streaming rows
- * and outputs when the call writes at least 4 MiB of results, streaming rows
- * alone when it may gather at least 64 MiB, else cached (thresholds set by
- * measurement on MI355X). */
+ * when the call writes at least 4 MiB of results or may gather at least 64 MiB;
+ * streaming outputs too when that is one part of at least 4 MiB (several parts
+ * are read back by the combine kernel and stay cached); else cached
+ * (thresholds set by measurement on MI355X). */
 typedef enum {
     SMLA_CACHE_AUTO = 0,
     SMLA_CACHE_CACHED = 1,          /* rows and outputs through the caches as ordinary accesses */

@@ -68,10 +68,10 @@ PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_pa
 # by the partial kernel, streaming rows alone from 64 MiB of gathered rows (upper bound rows * topk * row
 # bytes), else cached
 PLANNED_POLICY = {"b1_topk512_n4096_contiguous_bf16": B.CACHE_CACHED, "b1_topk2048_n32768_paged_bf16": B.CACHE_CACHED,
-                  "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_BOTH,
-                  "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_BOTH,
+                  "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_ROWS,
+                  "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_ROWS,
                   "b128_q2_topk2048_n65536_paged_fp8": B.CACHE_STREAM_BOTH,
-                  "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_BOTH}
+                  "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_ROWS}
 
 
 @pytest.mark.parametrize("w", I.WORKLOADS, ids=lambda w: w.name)
@@ -96,6 +96,13 @@ def test_plan_cache_policy_thresholds():
     assert out.cache_policy == B.CACHE_STREAM_BOTH
     out_below = B.decode_plan(63, 1, 32, 64, num_cus=256, force_splits=1)  # 4 MiB - 64 KiB out
     assert out_below.cache_policy == B.CACHE_CACHED
+    # several parts: the parts stay cached for the combine; rows streamed from 4 MiB of parts
+    parts = B.decode_plan(32, 1, 64, 64, num_cus=256, force_splits=2)      # 2 x 32 parts: 4 MiB
+    assert parts.num_splits == 2 and parts.cache_policy == B.CACHE_STREAM_ROWS
+    parts_below = B.decode_plan(31, 1, 64, 64, num_cus=256, force_splits=2)
+    assert parts_below.cache_policy == B.CACHE_CACHED
+    many = B.decode_plan(29, 1, 2048, 64, num_cus=256, force_splits=2)     # 65.3 MiB rows, 3.6 MiB of parts
+    assert many.cache_policy == B.CACHE_STREAM_ROWS
     for bad in (-1, 5):
         with pytest.raises(B.SmlaError):
             B.decode_plan(1, 1, 64, 4, num_cus=256, cache_policy=bad)
