@@ -460,7 +460,6 @@ def bench_indexer(args) -> int:
     import numpy as np
     import torch
 
-    import oracle
     from sparse_mla_decode_smla_amd import binding as B
     from sparse_mla_decode_smla_amd import inputs as I
 
@@ -508,6 +507,7 @@ def bench_indexer(args) -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg only
         log("[bench] timing the oracle on the host")
         t0 = time.perf_counter()
         reps = 0
