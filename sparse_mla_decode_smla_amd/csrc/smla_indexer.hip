@@ -80,7 +80,16 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
                                                                   const int32_t* __restrict__ block_table,
                                                                   const int32_t* __restrict__ seq_lens, int q_len,
                                                                   int max_blocks, float* __restrict__ scores) {
-    const int b = blockIdx.y;
+    // (sequence, chunk) items dealt XCD by XCD: consecutive workgroup ids go
+    // round-robin over the 8 XCDs, XCD x takes the x-th eighth of the items, so
+    // a sequence's scores land in the L2 of the XCD whose select workgroups read
+    // them (the select kernel deals its rows the same way)
+    const int nchunk = (max_blocks + kScoreWaves * kBlocksPerWave - 1) / (kScoreWaves * kBlocksPerWave);
+    const int nitems = (int)gridDim.x;
+    const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int item = xcd * (nitems >> 3) + min(xcd, nitems & 7) + within;
+    const int b = item / nchunk;
+    const int chunk = item - b * nchunk;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;   // token within a group of 4
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
 
 #pragma unroll 1
     for (int i = 0; i < kBlocksPerWave; ++i) {
-        const int j = (blockIdx.x * kBlocksPerWave + i) * kScoreWaves + wave;  // logical block
+        const int j = (chunk * kBlocksPerWave + i) * kScoreWaves + wave;  // logical block
         if (j >= max_blocks || j * kBlk >= n) continue;
         const int blk = block_table[(int64_t)b * max_blocks + j];
         const int tok_end = min(kBlk, n - j * kBlk);
@@ -192,7 +201,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     __shared__ unsigned res_sh[3];
     __shared__ int cand_n;
 
-    const int r = blockIdx.x;
+    const int nr = (int)gridDim.x, xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int r = xcd * (nr >> 3) + min(xcd, nr & 7) + within;  // rows dealt as the score kernel deals sequences
     const int b = r / q_len;
     const int tid = threadIdx.x;
     const int64_t cap = (int64_t)kBlk * max_blocks;
@@ -418,7 +428,7 @@ smla_status_t launch_scores(const void* q_idx, const void* k_cache, int64_t num_
                             const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t q_len,
                             int32_t max_blocks_per_seq, float* scores, hipStream_t st) {
     const int per_wg = kScoreWaves * kBlocksPerWave;
-    dim3 g1((unsigned)((max_blocks_per_seq + per_wg - 1) / per_wg), (unsigned)batch);
+    dim3 g1((unsigned)((max_blocks_per_seq + per_wg - 1) / per_wg) * (unsigned)batch);
     auto launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, g1, dim3(64 * kScoreWaves), 0, st, (const uint16_t*)q_idx,
                            (const uint8_t*)k_cache, num_kv_blocks, block_table, seq_lens, (int)q_len,
