@@ -270,16 +270,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         constexpr int kMaxBtInLds = 4096;
         static_assert(kMaxBtInLds * 4 <= NST * STAGE, "block-table copy exceeds the stage ring");
         const bool bt_in_lds = a.max_blocks <= kMaxBtInLds;
-        // 64-entry chunks, chunk c by PV wave c % 4; lane l copies entry 64c + l
-        // (lanes past the end copy nothing; index-list entries past nk are -1)
-        if (bt_in_lds)
-            for (int c = pw; 64 * c < a.max_blocks; c += 4)
-                if (64 * c + lane < a.max_blocks) lds_dma4(bt + 64 * c + lane, lds0 + 256u * c);
+        // Whole 256-entry chunks of a 16-byte aligned row by 16-byte LDS-DMA (lane
+        // l copies entries 4l .. 4l + 3), chunk c by PV wave c % 4; the rest in
+        // 64-entry chunks, one entry per lane (lanes past the end copy nothing;
+        // index-list entries past nk are -1).
+        if (bt_in_lds) {
+            const int full = ((uintptr_t)bt & 15) == 0 ? a.max_blocks / 256 : 0;
+            for (int c = pw; c < full; c += 4) lds_dma16<false>(bt + 256 * c + 4 * lane, lds0 + 1024u * c);
+            for (int c = pw; 256 * full + 64 * c < a.max_blocks; c += 4) {
+                const int e = 256 * full + 64 * c + lane;
+                if (e < a.max_blocks) lds_dma4(bt + e, lds0 + 4u * (256 * full + 64 * c));
+            }
+        }
         const unsigned rt0 = (unsigned)(uintptr_t)rowtab;
-        for (int c = pw; 64 * c < nent; c += 4) {
-            const int i = 64 * c + lane;
+        const int full_i = ((uintptr_t)idx & 15) == 0 ? nk / 256 : 0;
+        for (int c = pw; c < full_i; c += 4) lds_dma16<false>(idx + 256 * c + 4 * lane, rt0 + 1024u * c);
+        for (int c = pw; 256 * full_i + 64 * c < nent; c += 4) {
+            const int i = 256 * full_i + 64 * c + lane;
             if (i < nk)
-                lds_dma4(idx + i, rt0 + 256u * c);
+                lds_dma4(idx + i, rt0 + 4u * (256 * full_i + 64 * c));
             else if (i < nent)
                 *(__attribute__((address_space(3))) int*)(rowtab + 4 * i) = -1;
         }
