@@ -299,7 +299,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         wait_vmcnt<0>();
         __syncthreads();  // T1
         __attribute__((address_space(3))) int* const rt = (__attribute__((address_space(3))) int*)rowtab;
-        if (bt_in_lds) {
+        if (bt_in_lds && nent > 256) {
+            // 4 lookups in flight per lane, so a round of LDS reads costs one round
+            // trip for up to 1024 entries (lanes past the end read entry i0 and
+            // discard it)
+            const __attribute__((address_space(3))) int* btl = (const __attribute__((address_space(3))) int*)lds;
+            for (int i0 = pt; i0 < nent; i0 += 4 * 256) {
+                int pos[4], blk[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = i0 + 256 * j;
+                    pos[j] = rt[i < nent ? i : i0];
+                    if (!(i < nent && pos[j] >= 0 && (int64_t)pos[j] < cap)) pos[j] = -1;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) blk[j] = btl[pos[j] >= 0 ? pos[j] / kBlock : 0];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = i0 + 256 * j;
+                    if (i < nent)
+                        rt[i] = pos[j] >= 0 && blk[j] >= 0 && (int64_t)blk[j] < a.num_kv_blocks
+                                    ? blk[j] * kBlock + (pos[j] % kBlock)
+                                    : -1;
+                }
+            }
+        } else if (bt_in_lds) {
             const __attribute__((address_space(3))) int* btl = (const __attribute__((address_space(3))) int*)lds;
             for (int i = pt; i < nent; i += 256) {
                 const int pos = rt[i];
