@@ -88,14 +88,17 @@ def test_small_parity(fmt, splits):
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
-def test_masking_edge_cases(fmt):
-    inp = I.small_inputs(batch=4, q_len=2, topk=100, seq_len=600, kv_format=fmt, seed=21 + fmt)
+@pytest.mark.parametrize("topk,seq_len", [(100, 600), (700, 1500)], ids=["topk100", "topk700"])
+def test_masking_edge_cases(fmt, topk, seq_len):
+    # top-k 700 in one part: 704 row-table entries, translated four per lane at a time
+    # (the last round ragged), with the same masked entries as the short lists
+    inp = I.small_inputs(batch=4, q_len=2, topk=topk, seq_len=seq_len, kv_format=fmt, seed=21 + fmt + topk)
     w = inp.workload
     rng = np.random.default_rng(5)
     idx = inp.indices.copy()
     cap = 64 * inp.block_table.shape[1]
     # row (0,0): scattered -1, negatives and positions past the table
-    pos = rng.choice(100, size=40, replace=False)
+    pos = rng.choice(topk, size=40, replace=False)
     idx[0, 0, pos[:15]] = -1
     idx[0, 0, pos[15:30]] = -123
     idx[0, 0, pos[30:]] = cap + 5
@@ -106,7 +109,7 @@ def test_masking_edge_cases(fmt):
     bt = inp.block_table.copy()
     bt[2, 3] = -4                                    # bad block ids mask their positions
     bt[3, 1] = inp.kv_cache.shape[0] + 9
-    note(f"masking edge cases fmt={fmt}")
+    note(f"masking edge cases fmt={fmt} topk={topk}")
     ref_o, ref_l = oracle.default().sparse_mla_decode(inp.q, inp.kv_cache, bt, idx, inp.seq_lens,
                                                       inp.softmax_scale, d_v=w.d_v, kv_format=fmt,
                                                       block_size=64, threads=8)
