@@ -261,6 +261,9 @@ smla_status_t smla_combine(const void *part_out, const float *part_lse, int32_t 
  *   out_scores   fp32  [batch, q_len, topk] or NULL
  *   workspace    >= smla_indexer_workspace_size(...) bytes, 16-byte aligned:
  *                fp32 scores [batch * q_len, block_size * max_blocks_per_seq]
+ *                first; for rows of more than 16,384 positions it also holds
+ *                the selection's per-chunk histograms, counts and candidate
+ *                lists (about 2.5x the scores in all)
  * For row (b, s) the candidates are the positions p < min(seq_lens[b],
  * block_size * max_blocks_per_seq) whose block-table entry lies in
  * [0, num_kv_blocks); score(p) = q_idx[b, s, :] . key(p), bf16 products
@@ -271,9 +274,10 @@ smla_status_t smla_combine(const void *part_out, const float *part_lse, int32_t 
  * Supported: d_idx = 128, block_size = 64, 1 <= q_len <= 4,
  * 0 <= topk <= 2048 (else SMLA_ERR_UNSUPPORTED).  Pointer alignment: q_idx
  * and k_cache 16 bytes, the int32/fp32 arrays 4 bytes (else
- * SMLA_ERR_INVALID_ARG).  Two kernels on `stream` (scores, then the
- * selection); asynchronous; allocates nothing; the launch geometry depends
- * only on the sizes.
+ * SMLA_ERR_INVALID_ARG).  Kernels on `stream`: the scores, then the
+ * selection (one kernel, or three when block_size * max_blocks_per_seq
+ * exceeds 16,384); asynchronous; allocates nothing; the launch geometry
+ * depends only on the sizes.
  */
 smla_status_t smla_indexer_workspace_size(int32_t batch, int32_t q_len, int32_t block_size,
                                           int32_t max_blocks_per_seq, uint64_t *bytes_out);

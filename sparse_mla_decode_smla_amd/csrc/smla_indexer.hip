@@ -15,7 +15,7 @@
 // min(topk, #candidates) positions of highest score (equal scores: lower
 // positions first), in ascending position order, then -1.
 //
-// Two kernels:
+// Two kernels (four for rows of more than 16,384 positions):
 //   score_kernel  streams each sequence's keys once (whole 64-token blocks,
 //                 16 KB contiguous) for all q_len rows of the sequence; a
 //                 token's 256-byte key is spread over 16 lanes (16 bytes
@@ -24,15 +24,18 @@
 //                 streaming, not a contraction worth the matrix cores (one or
 //                 two query rows per key).
 //   select_kernel one 1024-thread workgroup per row, each thread owning a
-//                 contiguous run of positions (held in registers for rows of
-//                 up to 65536 positions): an exact radix select of the
-//                 topk-th largest score over an order-preserving key (digits
-//                 of 12, 12 and 8 bits, LDS histogram of 4096 bins; after the
-//                 first digit only the keys in its bin, copied to LDS, take
-//                 part), then one block scan that gives every thread its
-//                 output slots, so the winners (and the lowest positions of
-//                 the threshold's ties) are written in ascending position
-//                 order with no sort.
+//                 contiguous run of up to 16 positions held in registers: an
+//                 exact radix select of the topk-th largest score over an
+//                 order-preserving key (digits of 12, 12 and 8 bits, LDS
+//                 histogram of 4096 bins; after the first digit only the keys
+//                 in its bin, copied to LDS, take part), then one block scan
+//                 that gives every thread its output slots, so the winners
+//                 (and the lowest positions of the threshold's ties) are
+//                 written in ascending position order with no sort.
+//   Longer rows take the same selection spread over one workgroup per 4096
+//   positions in three kernels (chunk_hist_kernel, chunk_thresh_kernel,
+//   chunk_final_kernel, below): a single workgroup reading a row of 65,536
+//   scores is bound by its own request rate.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,7 +53,6 @@ constexpr int kScoreWaves = 4;    // waves per score workgroup
 constexpr int kBlocksPerWave = 2; // cache blocks per wave per workgroup
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRegPer = 64;       // most positions per select thread held in registers
 constexpr int kBins = 4096;       // radix histogram bins (12-bit digits)
 constexpr int kCandCap = 4096;    // keys sharing the first digit kept in LDS
 constexpr unsigned kNegInfKey = 0x007FFFFFu;  // order key of -inf
@@ -154,8 +156,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
     }
 }
 
-// Block-wide exclusive scan of one value per thread (1024 threads); returns
-// the exclusive prefix and writes the total to *total.  `tmp` holds kSelWaves ints.
+// Block-wide exclusive scan of one value per thread (NW waves); returns the
+// exclusive prefix and writes the total to *total.  `tmp` holds NW ints.
+template <int NW = kSelWaves>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
@@ -167,7 +170,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
     if (lane == 63) tmp[wave] = x;
     __syncthreads();
     int wsum = 0, all = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const int t = tmp[w];
         if (w < wave) wsum += t;
         all += t;
@@ -178,10 +181,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
 }
 
 // grid (rows), kSelThreads threads.  Thread t owns the contiguous positions
-// [t * per, t * per + per) of its row, so one block scan orders the output by
-// position.  PER > 0: per = PER and the row's keys stay in registers (rows of
-// up to PER * kSelThreads positions); PER = 0: every pass streams the
-// thread's positions from the workspace.
+// [t * PER, t * PER + PER) of its row, their keys held in registers, so one
+// block scan orders the output by position (rows of up to kChunkedFrom
+// positions; longer rows take the chunked selection below).
 //
 // Radix select over digits of 12, 12 and 8 bits.  The first digit of a key
 // is its top 12 bits; keys of non-candidates (<= kNegInfKey) land in digits
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                                                              const int32_t* __restrict__ seq_lens, int q_len,
                                                              int max_blocks, int topk, int32_t* __restrict__ out_idx,
                                                              float* __restrict__ out_score) {
-    constexpr bool REG = PER > 0;
+    static_assert(PER > 0 && PER <= 64, "a thread's keys are held in registers");
     __shared__ unsigned hist[kBins];
     __shared__ unsigned cand[kCandCap];
     __shared__ int scan_tmp[kSelWaves];
@@ -208,43 +210,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     const int64_t cap = (int64_t)kBlk * max_blocks;
     const int n = (int)min((int64_t)max(seq_lens[b], 0), cap);
     const float* s = scores + (int64_t)r * cap;
-    const int per = REG ? PER : (((n + kSelThreads - 1) / kSelThreads + 3) & ~3);
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    const int lo = min(n, tid * PER), hi = min(n, lo + PER);
     const bool mine_any = lo < hi;
 
     // keys of this thread's positions; 0 (a non-candidate key) past hi
-    unsigned keys[REG ? PER : 1];
-    if (REG) {
+    unsigned keys[PER];
 #pragma unroll
-        for (int j = 0; j < PER; j += 4) {
-            const int p = lo + j;  // a multiple of 4: a load that starts below n stays in the row
-            const f32x4 v = p < hi ? *(const f32x4*)(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < PER; j += 4) {
+        const int p = lo + j;  // a multiple of 4: a load that starts below n stays in the row
+        const f32x4 v = p < hi ? *(const f32x4*)(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) keys[j + e] = p + e < hi ? order_key(v[e]) : 0u;
-        }
+        for (int e = 0; e < 4; ++e) keys[j + e] = p + e < hi ? order_key(v[e]) : 0u;
     }
-    // f(position, key) over this thread's positions (streamed for PER = 0)
+    // f(position, key) over this thread's positions (those past hi carry key 0)
     auto for_mine = [&](auto f) {
-        if (REG) {
 #pragma unroll
-            for (int j = 0; j < (REG ? PER : 1); ++j) f(lo + j, keys[j]);
-        } else {
-            for (int p0 = lo; p0 < hi; p0 += 16) {
-                f32x4 v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int p = p0 + 4 * u;
-                    v[u] = p < hi ? *(const f32x4*)(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int p = p0 + 4 * u + e;
-                        if (p < hi) f(p, order_key(v[u][e]));
-                    }
-            }
-        }
+        for (int j = 0; j < PER; ++j) f(lo + j, keys[j]);
     };
     // the digit of the `remaining`-th largest key in the histogram: thread t
     // holds the counts of digits dmask - 4t .. dmask - 4t - 3 (largest first);
@@ -329,65 +310,415 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
         // those equal to it, written in position order
         const unsigned tau = prefix;
         const int need_eq = remaining;
-        int ngt = 0, neq = 0;
-        unsigned long long mg = 0, me = 0;  // REG: this thread's keys above / equal to tau
-        if (REG) {
+        unsigned long long mg = 0, me = 0;  // this thread's keys above / equal to tau
 #pragma unroll
-            for (int jj = 0; jj < (REG ? PER : 1); ++jj) {
-                mg |= (unsigned long long)(keys[jj] > tau) << jj;
-                me |= (unsigned long long)(keys[jj] == tau) << jj;
-            }
-            ngt = __builtin_popcountll(mg);
-            neq = __builtin_popcountll(me);
-        } else if (mine_any) {
-            for_mine([&](int, unsigned k) {
-                ngt += k > tau;
-                neq += k == tau;
-            });
+        for (int jj = 0; jj < PER; ++jj) {
+            mg |= (unsigned long long)(keys[jj] > tau) << jj;
+            me |= (unsigned long long)(keys[jj] == tau) << jj;
         }
+        const int ngt = __builtin_popcountll(mg), neq = __builtin_popcountll(me);
         int tot;
         const int gt_before = block_exclusive_scan(ngt, scan_tmp, &tot);
         int eq_rank = block_exclusive_scan(neq, scan_tmp, &tot);
         int j = gt_before + min(eq_rank, need_eq);
-        if (REG) {
-            // the keys above tau and the lowest of this thread's ties still wanted,
-            // one store per set bit (the scores are read back from the row; -0 is
-            // reported as +0)
-            unsigned long long take = mg;
-            for (int c = max(0, min(neq, need_eq - eq_rank)); c > 0; --c) {
-                const unsigned long long low = me & (~me + 1ull);
-                take |= low;
-                me ^= low;
+        // the keys above tau and the lowest of this thread's ties still wanted,
+        // one store per set bit (the scores are read back from the row; -0 is
+        // reported as +0)
+        unsigned long long take = mg;
+        for (int c = max(0, min(neq, need_eq - eq_rank)); c > 0; --c) {
+            const unsigned long long low = me & (~me + 1ull);
+            take |= low;
+            me ^= low;
+        }
+        while (take) {
+            const int jj = __builtin_ctzll(take);
+            take &= take - 1;
+            oi[j] = lo + jj;
+            if (os) {
+                const float v = s[lo + jj];
+                os[j] = v == 0.f ? 0.f : v;
             }
-            while (take) {
-                const int jj = __builtin_ctzll(take);
-                take &= take - 1;
-                oi[j] = lo + jj;
-                if (os) {
-                    const float v = s[lo + jj];
-                    os[j] = v == 0.f ? 0.f : v;
-                }
-                ++j;
-            }
-        } else if (mine_any) {
-            for_mine([&](int p, unsigned k) {
-                bool take = k > tau;
-                if (k == tau) {
-                    take = eq_rank < need_eq;
-                    ++eq_rank;
-                }
-                if (take) {
-                    oi[j] = p;
-                    if (os) os[j] = key_score(k);
-                    ++j;
-                }
-            });
+            ++j;
         }
     }
     for (int j = kk + tid; j < topk; j += kSelThreads) {
         oi[j] = -1;
         if (os) os[j] = -INFINITY;
     }
+}
+
+
+// ---- chunked selection: rows of more than kChunkedFrom positions
+//
+// One workgroup of 256 threads per (row, chunk of kChunk positions), thread t
+// owning the 16 contiguous positions kChunk c + 16 t ..; three kernels, with
+// no atomics between workgroups (each kernel reads what the previous one
+// wrote):
+//   chunk_hist_kernel   the chunk's histogram of the first 12-bit digit of
+//                       its candidates' keys (u16 counts) and, from it, of
+//                       the top 8 bits (16 first digits each);
+//   chunk_thresh_kernel every workgroup of a row sums the row's histograms:
+//                       the top 8 bits of the kk-th largest key from the
+//                       coarse counts, then its first digit T from the 16
+//                       fine counts under them; the keys above T and with
+//                       digit T in the chunks before its own, and the
+//                       chunk's keys with digit T appended, in position
+//                       order, to the row's candidate list;
+//   chunk_final_kernel  every workgroup of a row finds the last two digits
+//                       of the kk-th largest key from the candidate list
+//                       (usually a few hundred keys), counts the list's
+//                       entries of the earlier chunks above and equal to it,
+//                       and writes its chunk's winners at their slots.
+// The winners and their order are those of select_kernel.
+constexpr int kChunk = 4096;
+constexpr int kChThreads = 256;
+constexpr int kChWaves = kChThreads / 64;
+constexpr int kChPer = kChunk / kChThreads;        // positions per thread
+constexpr int kCoarseBins = 256;                   // top 8 bits of a key
+constexpr int kHistU16 = kCoarseBins + kBins;      // per chunk: coarse counts, then first-digit counts
+constexpr int kChunkedFrom = 16 * kSelThreads;     // rows of up to this many positions: select_kernel
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// (row, chunk) of this workgroup: items r * nch_max + c dealt XCD by XCD, as
+// the score kernel deals a sequence's items, so a row's chunks and scores
+// share an L2
+__device__ __forceinline__ void chunk_item(int nch_max, int& r, int& c) {
+    const int nitems = (int)gridDim.x, xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int item = xcd * (nitems >> 3) + min(xcd, nitems & 7) + within;
+    r = item / nch_max;
+    c = item - r * nch_max;
+}
+
+// this thread's 16 keys of chunk c of a row with n positions (0, a
+// non-candidate key, past n)
+__device__ __forceinline__ void chunk_keys(const float* s, int c, int n, unsigned (&k)[kChPer]) {
+    const int p0 = c * kChunk + kChPer * (int)threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kChPer; j += 4) {
+        const int p = p0 + j;  // a multiple of 4: a load that starts below n stays in the row
+        const f32x4 v = p < n ? *(const f32x4*)(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ve = v[e];
+            k[j + e] = p + e < n ? order_key(ve) : 0u;
+        }
+    }
+}
+
+// positions of row r and its number of chunks
+__device__ __forceinline__ int row_positions(const int32_t* seq_lens, int r, int q_len, int64_t cap) {
+    return (int)min((int64_t)max(seq_lens[r / q_len], 0), cap);
+}
+
+// sum of a histogram entry (at h, stride kHistU16) over the chunks [0, nch),
+// and over [0, c): the loads are issued 16 at a time before they are used
+__device__ __forceinline__ void sum_chunks(const uint16_t* h, int nch, int c, int& all, int& before) {
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+        int v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = h[(int64_t)min(c0 + j, nch - 1) * kHistU16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int x = c0 + j < nch ? v[j] : 0;
+            all += x;
+            before += c0 + j < c ? x : 0;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kChThreads) void chunk_hist_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ seq_lens, int q_len,
+                                                                int max_blocks, int nch_max,
+                                                                uint16_t* __restrict__ hist) {
+    __shared__ unsigned hf[kBins];
+    int r, c;
+    chunk_item(nch_max, r, c);
+    const int64_t cap = (int64_t)kBlk * max_blocks;
+    const int n = row_positions(seq_lens, r, q_len, cap);
+    if (c * kChunk >= n) return;  // no such chunk: nothing reads its histogram
+    const int tid = threadIdx.x;
+    unsigned k[kChPer];
+    chunk_keys(scores + (int64_t)r * cap, c, n, k);
+    for (int i = tid; i < kBins; i += kChThreads) hf[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kChPer; ++j)
+        if (k[j] > kNegInfKey) atomicAdd(&hf[k[j] >> 20], 1u);
+    __syncthreads();
+    // thread t: first digits 16t .. 16t + 15, whose sum is the count of top-8-bit value t
+    uint16_t* h = hist + ((int64_t)r * nch_max + c) * kHistU16;
+    u16x8 lo, hi;
+    unsigned coarse = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const unsigned a = hf[16 * tid + e], b = hf[16 * tid + 8 + e];
+        lo[e] = (unsigned short)a;
+        hi[e] = (unsigned short)b;
+        coarse += a + b;
+    }
+    h[tid] = (uint16_t)coarse;
+    *(u16x8*)(h + kCoarseBins + 16 * tid) = lo;
+    *(u16x8*)(h + kCoarseBins + 16 * tid + 8) = hi;
+}
+
+__global__ __launch_bounds__(kChThreads) void chunk_thresh_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ seq_lens, int q_len,
+                                                                  int max_blocks, int nch_max, int topk,
+                                                                  const uint16_t* __restrict__ hist,
+                                                                  int* __restrict__ cinfo, int* __restrict__ header,
+                                                                  unsigned* __restrict__ cand) {
+    __shared__ int scan_tmp[kChWaves];
+    __shared__ int sh[5];
+    __shared__ int sh_fb[64];
+    int r, c;
+    chunk_item(nch_max, r, c);
+    const int64_t cap = (int64_t)kBlk * max_blocks;
+    const int n = row_positions(seq_lens, r, q_len, cap);
+    const int nch = (n + kChunk - 1) / kChunk;
+    if (c >= max(nch, 1)) return;  // chunk 0 writes the row's header even for an empty row
+    const int tid = threadIdx.x;
+    unsigned k[kChPer];
+    if (c < nch) chunk_keys(scores + (int64_t)r * cap, c, n, k);
+    const uint16_t* hr = hist + (int64_t)r * nch_max * kHistU16;
+
+    // coarse counts over the row, largest top-8-bit value first (thread t: value
+    // 255 - t), and over the chunks before this one; loads issued 16 at a time
+    const int cb = kCoarseBins - 1 - tid;
+    int tot = 0, before_cb = 0;
+    sum_chunks(hr + cb, nch, c, tot, before_cb);
+    int ncand;
+    const int above = block_exclusive_scan<kChWaves>(tot, scan_tmp, &ncand);
+    const int kk = min(topk, ncand);
+    if (kk == 0) {
+        if (c == 0 && tid == 0) {
+            header[4 * r + 0] = 0;
+            header[4 * r + 1] = 0;
+            header[4 * r + 2] = 0;
+            header[4 * r + 3] = 0;
+        }
+        return;
+    }
+    if (above < kk && above + tot >= kk) {
+        sh[0] = cb;
+        sh[1] = above;
+    }
+    __syncthreads();
+    const int ct = sh[0], above_c = sh[1];
+    // the 16 first digits under it (lane t < 16: digit 16 ct + 15 - t), in the first wave
+    if (tid < 64) {
+        const int fd = 16 * ct + 15 - (tid & 15);
+        int ft = 0, fb = 0;
+        if (tid < 16) sum_chunks(hr + kCoarseBins + fd, nch, c, ft, fb);
+        sh_fb[tid] = fb;
+        int x = ft;  // inclusive prefix over lanes 0..15
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if ((tid & 15) >= o) x += y;
+        }
+        const int want = kk - above_c, acc = x - ft;
+        if (tid < 16 && acc < want && acc + ft >= want) {
+            sh[2] = fd;
+            sh[3] = above_c + acc;
+            sh[4] = ft;
+        }
+    }
+    __syncthreads();
+    const int T = sh[2], gt_total = sh[3];
+    if (c == 0 && tid == 0) {
+        header[4 * r + 0] = T;
+        header[4 * r + 1] = gt_total;
+        header[4 * r + 2] = sh[4];
+        header[4 * r + 3] = kk;
+    }
+    if (c >= nch) return;
+
+    // keys above T and keys with digit T in the chunks before this one
+    int gtb = cb > ct ? before_cb : 0, cbe = 0;
+    if (tid < 16) {
+        const int fd = 16 * ct + 15 - tid;
+        if (fd > T) gtb += sh_fb[tid];
+        if (fd == T) cbe = sh_fb[tid];
+    }
+    int gt_before, cand_before;
+    (void)block_exclusive_scan<kChWaves>(gtb, scan_tmp, &gt_before);
+    (void)block_exclusive_scan<kChWaves>(cbe, scan_tmp, &cand_before);
+
+    // this chunk's keys with digit T, appended in position order
+    int nt = 0;
+#pragma unroll
+    for (int j = 0; j < kChPer; ++j) nt += (k[j] >> 20) == (unsigned)T;
+    int dummy;
+    int o = cand_before + block_exclusive_scan<kChWaves>(nt, scan_tmp, &dummy);
+    unsigned* cr = cand + (int64_t)r * cap;
+#pragma unroll
+    for (int j = 0; j < kChPer; ++j)
+        if ((k[j] >> 20) == (unsigned)T && o < n) cr[o++] = k[j];  // (o < n always holds)
+    if (tid == 0) {
+        cinfo[4 * ((int64_t)r * nch_max + c) + 0] = gt_before;
+        cinfo[4 * ((int64_t)r * nch_max + c) + 1] = cand_before;
+    }
+}
+
+__global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __restrict__ scores,
+                                                                 const int32_t* __restrict__ seq_lens, int q_len,
+                                                                 int max_blocks, int nch_max, int topk,
+                                                                 const int* __restrict__ cinfo,
+                                                                 const int* __restrict__ header,
+                                                                 const unsigned* __restrict__ cand,
+                                                                 int32_t* __restrict__ out_idx,
+                                                                 float* __restrict__ out_score) {
+    __shared__ unsigned hist[kBins];
+    __shared__ int scan_tmp[kChWaves];
+    __shared__ unsigned res_sh[2];
+    int r, c;
+    chunk_item(nch_max, r, c);
+    const int64_t cap = (int64_t)kBlk * max_blocks;
+    const int n = row_positions(seq_lens, r, q_len, cap);
+    const int nch = (n + kChunk - 1) / kChunk;
+    if (c >= max(nch, 1)) return;
+    const int tid = threadIdx.x;
+    // the chunk's keys, the row's header and the chunk's counts, all issued first
+    unsigned k[kChPer];
+    if (c < nch) chunk_keys(scores + (int64_t)r * cap, c, n, k);
+    const int T = header[4 * r + 0], gt_total = header[4 * r + 1], M = header[4 * r + 2], kk = header[4 * r + 3];
+    const int gtb = c < nch ? cinfo[4 * ((int64_t)r * nch_max + c) + 0] : 0;
+    const int cbe = c < nch ? cinfo[4 * ((int64_t)r * nch_max + c) + 1] : 0;
+    int32_t* oi = out_idx + (int64_t)r * topk;
+    float* os = out_score ? out_score + (int64_t)r * topk : nullptr;
+    if (c == 0)
+        for (int j = kk + tid; j < topk; j += kChThreads) {
+            oi[j] = -1;
+            if (os) os[j] = -INFINITY;
+        }
+    if (kk == 0 || c >= nch) return;
+    const unsigned* cr = cand + (int64_t)r * cap;
+    // the candidate list: entry tid + 256 j in cv[j] when the list has at most
+    // kCandRegs * 256 entries (usually a few hundred), else read from the
+    // workspace in every pass
+    constexpr int kCandRegs = 4;
+    const bool in_regs = M <= kCandRegs * kChThreads;
+    unsigned cv[kCandRegs];
+#pragma unroll
+    for (int j = 0; j < kCandRegs; ++j) {
+        const int i = tid + kChThreads * j;
+        cv[j] = in_regs && i < M ? cr[i] : 0u;
+    }
+    auto for_cand = [&](int upto, auto f) {
+        if (in_regs) {
+#pragma unroll
+            for (int j = 0; j < kCandRegs; ++j)
+                if (tid + kChThreads * j < upto) f(cv[j]);
+        } else {
+            for (int i = tid; i < upto; i += kChThreads) f(cr[i]);
+        }
+    };
+
+    // the last two digits (bits 8..19, then 0..7) of the remaining-th largest
+    // key among the M keys with first digit T
+    int remaining = kk - gt_total;
+    unsigned prefix = (unsigned)T << 20, pmask = 0xFFF00000u;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 8 : 0;
+        const int nb = pass == 0 ? kBins : 256;
+        for (int i = tid; i < nb; i += kChThreads) hist[i] = 0;
+        __syncthreads();
+        for_cand(M, [&](unsigned key) {
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        // thread t: digits nb - 1 - per t - j (largest first)
+        const int per = nb / kChThreads;
+        int h = 0;
+        for (int j = 0; j < per; ++j) h += (int)hist[nb - 1 - per * tid - j];
+        int total;
+        int acc = block_exclusive_scan<kChWaves>(h, scan_tmp, &total);
+        if (acc < remaining && acc + h >= remaining)
+            for (int j = 0; j < per; ++j) {
+                const int hj = (int)hist[nb - 1 - per * tid - j];
+                if (acc < remaining && acc + hj >= remaining) {
+                    res_sh[0] = (unsigned)(nb - 1 - per * tid - j);
+                    res_sh[1] = (unsigned)acc;
+                }
+                acc += hj;
+            }
+        __syncthreads();
+        prefix |= res_sh[0] << shift;
+        remaining -= (int)res_sh[1];
+        pmask |= (unsigned)(nb - 1) << shift;
+        __syncthreads();
+    }
+    const unsigned tau = prefix;
+    const int need_eq = remaining;
+
+    // the list's keys of the earlier chunks above and equal to tau
+    int g = 0, e = 0;
+    for_cand(cbe, [&](unsigned key) {
+        g += key > tau;
+        e += key == tau;
+    });
+    int gsum, esum;
+    (void)block_exclusive_scan<kChWaves>(g, scan_tmp, &gsum);
+    (void)block_exclusive_scan<kChWaves>(e, scan_tmp, &esum);
+
+    // this thread's winners: every key above tau, and the lowest positions of
+    // those equal to it while the row still wants them
+    unsigned mg = 0, me = 0;
+#pragma unroll
+    for (int j = 0; j < kChPer; ++j) {
+        mg |= (unsigned)(k[j] > tau) << j;
+        me |= (unsigned)(k[j] == tau) << j;
+    }
+    const int ngt = __builtin_popcount(mg), neq = __builtin_popcount(me);
+    int dummy;
+    const int gt_pre = block_exclusive_scan<kChWaves>(ngt, scan_tmp, &dummy);
+    const int eq_rank = esum + block_exclusive_scan<kChWaves>(neq, scan_tmp, &dummy);
+    int j = gtb + gsum + gt_pre + min(eq_rank, need_eq);
+    unsigned take = mg;
+    for (int t = max(0, min(neq, need_eq - eq_rank)); t > 0; --t) {
+        const unsigned low = me & (~me + 1u);
+        take |= low;
+        me ^= low;
+    }
+    // (a static loop over the 16 keys keeps them in registers; the score is
+    // the key's inverse, -0 reported as +0)
+    const int p0 = c * kChunk + kChPer * tid;
+#pragma unroll
+    for (int jj = 0; jj < kChPer; ++jj)
+        if (((take >> jj) & 1u) && j < kk) {  // (j < kk always holds)
+            oi[j] = p0 + jj;
+            if (os) os[j] = key_score(k[jj]);
+            ++j;
+        }
+}
+
+
+// Byte offsets in the workspace of smla_indexer_topk: the fp32 scores [rows,
+// cap], then for rows of more than kChunkedFrom positions the chunk histograms
+// (u16 [rows, nch, kHistU16]), the per-chunk counts (int [rows, nch, 4]), the
+// row headers (int [rows, 4]) and the candidate lists (u32 [rows, cap]); every
+// part starts 16-byte aligned.
+struct WsLayout {
+    uint64_t hist, cinfo, header, cand, total;
+};
+WsLayout ws_layout(int64_t rows, int64_t cap) {
+    WsLayout w{};
+    uint64_t off = (uint64_t)rows * (uint64_t)cap * 4u;
+    if (cap > kChunkedFrom) {
+        const uint64_t nch = (uint64_t)((cap + kChunk - 1) / kChunk);
+        w.hist = off;
+        off += (uint64_t)rows * nch * kHistU16 * 2u;
+        w.cinfo = off;
+        off += (uint64_t)rows * nch * 16u;
+        w.header = off;
+        off += (uint64_t)rows * 16u;
+        w.cand = off;
+        off += (uint64_t)rows * (uint64_t)cap * 4u;
+    }
+    w.total = off;
+    return w;
 }
 
 }  // namespace
@@ -397,7 +728,7 @@ extern "C" smla_status_t smla_indexer_workspace_size(int32_t batch, int32_t q_le
                                                      int32_t max_blocks_per_seq, uint64_t* bytes_out) {
     if (!bytes_out || batch < 0 || q_len < 1 || block_size < 1 || max_blocks_per_seq < 1)
         return SMLA_ERR_INVALID_ARG;
-    *bytes_out = (uint64_t)batch * (uint64_t)q_len * (uint64_t)block_size * (uint64_t)max_blocks_per_seq * 4u;
+    *bytes_out = smla_idx::ws_layout((int64_t)batch * q_len, (int64_t)block_size * max_blocks_per_seq).total;
     return SMLA_OK;
 }
 
@@ -477,9 +808,12 @@ extern "C" smla_status_t smla_indexer_topk(const void* q_idx, int32_t d_idx, con
     if (batch == 0 || topk == 0) return SMLA_OK;
     if (!out_indices || ((uintptr_t)out_indices & 3) || ((uintptr_t)out_scores & 3)) return SMLA_ERR_INVALID_ARG;
     const int64_t rows = (int64_t)batch * q_len;
-    const uint64_t need = (uint64_t)rows * (uint64_t)kBlk * (uint64_t)max_blocks_per_seq * 4u;
-    if (!workspace || workspace_bytes < need) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t cap = (int64_t)kBlk * max_blocks_per_seq;
+    const WsLayout wl = ws_layout(rows, cap);
+    if (!workspace || workspace_bytes < wl.total) return SMLA_ERR_WORKSPACE_TOO_SMALL;
     if ((uintptr_t)workspace & 15) return SMLA_ERR_INVALID_ARG;
+    const int64_t nch = (cap + kChunk - 1) / kChunk;
+    if (cap > kChunkedFrom && rows * nch > INT32_MAX) return SMLA_ERR_UNSUPPORTED;
 
     (void)hipGetLastError();
     hipStream_t hs = (hipStream_t)stream;
@@ -487,22 +821,32 @@ extern "C" smla_status_t smla_indexer_topk(const void* q_idx, int32_t d_idx, con
     st = launch_scores(q_idx, k_cache, num_kv_blocks, block_table, seq_lens, batch, q_len, max_blocks_per_seq,
                        scores, hs);
     if (st != SMLA_OK) return st;
-    // rows of up to kRegPer * kSelThreads positions keep their scores in
-    // registers, PER of them per thread (the smallest that covers the row)
-    const int64_t cap = (int64_t)kBlk * max_blocks_per_seq;
+    if (cap > kChunkedFrom) {
+        // long rows: chunk histograms, threshold digit and candidate lists, then the winners
+        uint8_t* wb = (uint8_t*)workspace;
+        uint16_t* hist = (uint16_t*)(wb + wl.hist);
+        int* cinfo = (int*)(wb + wl.cinfo);
+        int* header = (int*)(wb + wl.header);
+        unsigned* cand = (unsigned*)(wb + wl.cand);
+        const dim3 g((unsigned)(rows * nch)), t(kChThreads);
+        hipLaunchKernelGGL(chunk_hist_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
+                           (int)nch, hist);
+        hipLaunchKernelGGL(chunk_thresh_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
+                           (int)nch, (int)topk, hist, cinfo, header, cand);
+        hipLaunchKernelGGL(chunk_final_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
+                           (int)nch, (int)topk, cinfo, header, cand, out_indices, out_scores);
+        return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+    }
+    // shorter rows keep their scores in registers, PER of them per thread (the
+    // smallest that covers the row)
     auto launch = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, hs, scores, seq_lens, (int)q_len,
                            (int)max_blocks_per_seq, (int)topk, out_indices, out_scores);
     };
+    static_assert(kChunkedFrom == 16 * kSelThreads, "select_kernel<16> covers every row up to kChunkedFrom");
     if (cap <= 8 * kSelThreads)
         launch(select_kernel<8>);
-    else if (cap <= 16 * kSelThreads)
-        launch(select_kernel<16>);
-    else if (cap <= 32 * kSelThreads)
-        launch(select_kernel<32>);
-    else if (cap <= (int64_t)kRegPer * kSelThreads)
-        launch(select_kernel<kRegPer>);
     else
-        launch(select_kernel<0>);
+        launch(select_kernel<16>);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }

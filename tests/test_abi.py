@@ -252,6 +252,11 @@ def test_combine_argument_checks_need_no_gpu():
 def test_indexer_argument_checks_need_no_gpu():
     lib = B.load()
     assert B.indexer_workspace_size(3, 2, 10) == 3 * 2 * 640 * 4
+    assert B.indexer_workspace_size(1, 1, 256) == 16384 * 4              # the one-kernel selection
+    # rows of more than 16,384 positions: scores, then per chunk of 4096 positions a histogram of 4352
+    # u16 counts and 16 bytes of counts, 16 bytes per row, and a candidate list as long as the row
+    rows, cap, nch = 2, 300 * 64, 5
+    assert B.indexer_workspace_size(2, 1, 300) == rows * cap * 4 + rows * nch * (4352 * 2 + 16) + rows * 16 + rows * cap * 4
     n = ctypes.c_uint64(0)
     assert lib.smla_indexer_workspace_size(-1, 1, 64, 10, ctypes.byref(n)) == 1
     assert lib.smla_indexer_workspace_size(1, 1, 64, 10, None) == 1
@@ -266,6 +271,8 @@ def test_indexer_argument_checks_need_no_gpu():
     assert call(topk=-1) == 1 and call(mb=0) == 1 and call(nb=-1) == 1
     assert call(q=None) == 1 and call(sl=None) == 1 and call(oi=None) == 1
     assert call(wsb=2 * 512 * 4 - 1) == 3 and call(ws=None) == 3
+    long_ws = B.indexer_workspace_size(2, 1, 300)                       # chunked selection: its buffers count
+    assert call(mb=300, wsb=long_ws - 1) == 3 and call(mb=300, wsb=2 * 300 * 64 * 4) == 3
     assert call(q=(1 << 20) + 8) == 1 and call(k=(1 << 21) + 4) == 1 and call(oi=(1 << 24) + 2) == 1
     assert call(B=0, q=None, oi=None) == 0 and call(topk=0, oi=None) == 0   # nothing to do
     assert call(topk=0, q=None) == 1                                          # still checked

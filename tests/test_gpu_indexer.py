@@ -137,6 +137,52 @@ def test_indexer_exact_ties_go_to_lower_positions():
     assert np.array_equal(idx, ref), "with exact ties the selection must be the oracle's"
 
 
+def _periodic_keys(inp, period):
+    """A copy of the key cache in which position p of every sequence holds the key of position p % period,
+    so every score value occurs many times, bit-identical in fp32."""
+    k2 = inp.k_cache.copy().reshape(-1, 128)
+    flat = inp.k_cache.reshape(-1, 128)
+    bt = inp.block_table
+    for b in range(bt.shape[0]):
+        p = np.arange(bt.shape[1] * 64)
+        phys = bt[b, p // 64].astype(np.int64) * 64 + p % 64
+        src = bt[b, (p % period) // 64].astype(np.int64) * 64 + (p % period) % 64
+        k2[phys] = flat[src]
+    return k2.reshape(inp.k_cache.shape)
+
+
+def test_indexer_chunked_ties_across_chunks():
+    # rows of 20480 (five whole chunks of 4096), 20481 (one position in a sixth) and 17000 positions,
+    # each score value repeated every 7 positions: the threshold's ties spread over every chunk, and the
+    # lowest positions among them must win, as in the oracle
+    inp = I.small_indexer_inputs(batch=3, q_len=1, topk=2048, seq_len=20481, seed=44)
+    sl = np.array([20480, 20481, 17000], dtype=np.int32)
+    inp2 = I.IndexerInputs(workload=inp.workload, q_idx=inp.q_idx, k_cache=_periodic_keys(inp, 7),
+                           block_table=inp.block_table, seq_lens=sl)
+    note(f"indexer chunked ties: seq_lens {sl.tolist()}")
+    idx, sc, ws = run_indexer(inp2, 2048)
+    check(inp2, 2048, idx, sc, ws, "chunked ties")
+    ref, _ = oracle.indexer_topk(inp2.q_idx, inp2.k_cache, inp2.block_table, inp2.seq_lens, 2048)
+    assert np.array_equal(idx, ref), "with exact ties the selection must be the oracle's"
+
+
+def test_indexer_chunked_masks_and_short_rows():
+    # rows long enough for the chunked selection: an empty row, a row with fewer candidates than the list
+    # (its last chunk one position long), bad block ids inside chunks
+    inp = I.small_indexer_inputs(batch=4, q_len=2, topk=1000, seq_len=18000, seed=45)
+    bt = inp.block_table.copy()
+    sl = inp.seq_lens.copy()
+    sl[0] = 0                                    # no candidates
+    sl[1] = 16385                                # five chunks, the last one position long
+    bt[1, 5:250] = -1                            # ... and most blocks masked: fewer candidates than topk
+    bt[2, 70] = -3                               # one bad block in the middle of chunk 1
+    bt[3, 0] = inp.k_cache.shape[0] + 7          # the first block past the cache
+    idx, sc, ws = run_indexer(inp, 1000, block_table=bt, seq_lens=sl)
+    assert np.all(idx[0] == -1) and np.all(np.isneginf(sc[0]))
+    assert np.all((idx[1] >= 0).sum(axis=1) == 5 * 64 + (16385 - 250 * 64))
+    check(inp, 1000, idx, sc, ws, "chunked masks", block_table=bt, seq_lens=sl)
+
+
 def test_indexer_rows_longer_than_registers():
     # more than 65536 positions per row: the selection streams the row from the workspace each pass
     inp = I.small_indexer_inputs(batch=2, q_len=1, topk=300, seq_len_range=(66000, 70000), seed=37)
