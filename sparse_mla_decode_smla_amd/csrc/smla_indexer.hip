@@ -60,6 +60,7 @@ constexpr unsigned kNegInfKey = 0x007FFFFFu;  // order key of -inf
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // fp32 -> unsigned key with the same order (larger score, larger key; -0
 // and +0 are the same score).
@@ -175,6 +176,39 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
         if (w < wave) wsum += t;
         all += t;
     }
+    __syncthreads();
+    *total = all;
+    return wsum + x - v;
+}
+
+// The same for four values per thread in one pass (one round of LDS traffic
+// and two barriers): returns the exclusive prefixes, writes the totals.
+// `tmp` holds 4 * NW ints.
+template <int NW>
+__device__ __forceinline__ i32x4 block_exclusive_scan4(i32x4 v, int* tmp, i32x4* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    i32x4 x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int xi = x[i];
+            const int y = __shfl_up(xi, o);
+            if (lane >= o) x[i] = xi + y;
+        }
+    }
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmp[4 * wave + i] = x[i];
+    __syncthreads();
+    i32x4 wsum = {0, 0, 0, 0}, all = {0, 0, 0, 0};
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tmp[4 * w + i];
+            if (w < wave) wsum[i] += t;
+            all[i] += t;
+        }
     __syncthreads();
     *total = all;
     return wsum + x - v;
@@ -468,7 +502,7 @@ __global__ __launch_bounds__(kChThreads) void chunk_thresh_kernel(const float* _
                                                                   const uint16_t* __restrict__ hist,
                                                                   int* __restrict__ cinfo, int* __restrict__ header,
                                                                   unsigned* __restrict__ cand) {
-    __shared__ int scan_tmp[kChWaves];
+    __shared__ int scan_tmp[4 * kChWaves];
     __shared__ int sh[5];
     __shared__ int sh_fb[64];
     int r, c;
@@ -541,9 +575,9 @@ __global__ __launch_bounds__(kChThreads) void chunk_thresh_kernel(const float* _
         if (fd > T) gtb += sh_fb[tid];
         if (fd == T) cbe = sh_fb[tid];
     }
-    int gt_before, cand_before;
-    (void)block_exclusive_scan<kChWaves>(gtb, scan_tmp, &gt_before);
-    (void)block_exclusive_scan<kChWaves>(cbe, scan_tmp, &cand_before);
+    i32x4 tot4;
+    (void)block_exclusive_scan4<kChWaves>(i32x4{gtb, cbe, 0, 0}, scan_tmp, &tot4);
+    const int gt_before = tot4[0], cand_before = tot4[1];
 
     // this chunk's keys with digit T, appended in position order
     int nt = 0;
@@ -570,7 +604,7 @@ __global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __
                                                                  int32_t* __restrict__ out_idx,
                                                                  float* __restrict__ out_score) {
     __shared__ unsigned hist[kBins];
-    __shared__ int scan_tmp[kChWaves];
+    __shared__ int scan_tmp[4 * kChWaves];
     __shared__ unsigned res_sh[2];
     int r, c;
     chunk_item(nch_max, r, c);
@@ -579,9 +613,18 @@ __global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __
     const int nch = (n + kChunk - 1) / kChunk;
     if (c >= max(nch, 1)) return;
     const int tid = threadIdx.x;
-    // the chunk's keys, the row's header and the chunk's counts, all issued first
+    // the chunk's keys, the row's header, the chunk's counts and the first
+    // kCandRegs * 256 entries of the row's candidate list (entry tid + 256 j in
+    // cv[j]; the list is usually a few hundred entries long, and a row has more
+    // than 16,384 positions, so these reads stay in its list), all issued first
     unsigned k[kChPer];
     if (c < nch) chunk_keys(scores + (int64_t)r * cap, c, n, k);
+    const unsigned* cr = cand + (int64_t)r * cap;
+    constexpr int kCandRegs = 4;
+    static_assert(kCandRegs * kChThreads <= kChunkedFrom, "the speculative list reads stay in the row");
+    unsigned cv[kCandRegs];
+#pragma unroll
+    for (int j = 0; j < kCandRegs; ++j) cv[j] = cr[tid + kChThreads * j];
     const int T = header[4 * r + 0], gt_total = header[4 * r + 1], M = header[4 * r + 2], kk = header[4 * r + 3];
     const int gtb = c < nch ? cinfo[4 * ((int64_t)r * nch_max + c) + 0] : 0;
     const int cbe = c < nch ? cinfo[4 * ((int64_t)r * nch_max + c) + 1] : 0;
@@ -593,18 +636,9 @@ __global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __
             if (os) os[j] = -INFINITY;
         }
     if (kk == 0 || c >= nch) return;
-    const unsigned* cr = cand + (int64_t)r * cap;
-    // the candidate list: entry tid + 256 j in cv[j] when the list has at most
-    // kCandRegs * 256 entries (usually a few hundred), else read from the
-    // workspace in every pass
-    constexpr int kCandRegs = 4;
+    // the candidate list from registers when it has at most kCandRegs * 256
+    // entries, else read from the workspace in every pass
     const bool in_regs = M <= kCandRegs * kChThreads;
-    unsigned cv[kCandRegs];
-#pragma unroll
-    for (int j = 0; j < kCandRegs; ++j) {
-        const int i = tid + kChThreads * j;
-        cv[j] = in_regs && i < M ? cr[i] : 0u;
-    }
     auto for_cand = [&](int upto, auto f) {
         if (in_regs) {
 #pragma unroll
@@ -659,12 +693,9 @@ __global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __
         g += key > tau;
         e += key == tau;
     });
-    int gsum, esum;
-    (void)block_exclusive_scan<kChWaves>(g, scan_tmp, &gsum);
-    (void)block_exclusive_scan<kChWaves>(e, scan_tmp, &esum);
-
     // this thread's winners: every key above tau, and the lowest positions of
-    // those equal to it while the row still wants them
+    // those equal to it while the row still wants them (one scan: the list's
+    // counts summed, this thread's counts' prefixes)
     unsigned mg = 0, me = 0;
 #pragma unroll
     for (int j = 0; j < kChPer; ++j) {
@@ -672,9 +703,11 @@ __global__ __launch_bounds__(kChThreads) void chunk_final_kernel(const float* __
         me |= (unsigned)(k[j] == tau) << j;
     }
     const int ngt = __builtin_popcount(mg), neq = __builtin_popcount(me);
-    int dummy;
-    const int gt_pre = block_exclusive_scan<kChWaves>(ngt, scan_tmp, &dummy);
-    const int eq_rank = esum + block_exclusive_scan<kChWaves>(neq, scan_tmp, &dummy);
+    i32x4 tot4;
+    const i32x4 pre = block_exclusive_scan4<kChWaves>(i32x4{g, e, ngt, neq}, scan_tmp, &tot4);
+    const int gsum = tot4[0], esum = tot4[1];
+    const int gt_pre = pre[2];
+    const int eq_rank = esum + pre[3];
     int j = gtb + gsum + gt_pre + min(eq_rank, need_eq);
     unsigned take = mg;
     for (int t = max(0, min(neq, need_eq - eq_rank)); t > 0; --t) {
