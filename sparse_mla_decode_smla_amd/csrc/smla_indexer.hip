@@ -440,7 +440,7 @@ __device__ __forceinline__ void chunk_keys(const float* s, int c, int n, unsigne
     }
 }
 
-// positions of row r and its number of chunks
+// positions of row r (its sequence's length, at most cap)
 __device__ __forceinline__ int row_positions(const int32_t* seq_lens, int r, int q_len, int64_t cap) {
     return (int)min((int64_t)max(seq_lens[r / q_len], 0), cap);
 }
