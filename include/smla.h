@@ -275,7 +275,7 @@ smla_status_t smla_combine(const void *part_out, const float *part_lse, int32_t 
  * 0 <= topk <= 2048 (else SMLA_ERR_UNSUPPORTED).  Pointer alignment: q_idx
  * and k_cache 16 bytes, the int32/fp32 arrays 4 bytes (else
  * SMLA_ERR_INVALID_ARG).  Kernels on `stream`: the scores, then the
- * selection (one kernel, or three when block_size * max_blocks_per_seq
+ * selection (one kernel, or two when block_size * max_blocks_per_seq
  * exceeds 16,384); asynchronous; allocates nothing; the launch geometry
  * depends only on the sizes.
  */

@@ -33,9 +33,9 @@
 //                 (and the lowest positions of the threshold's ties) are
 //                 written in ascending position order with no sort.
 //   Longer rows take the same selection spread over one workgroup per 4096
-//   positions in three kernels (chunk_hist_kernel, chunk_thresh_kernel,
-//   chunk_final_kernel, below): a single workgroup reading a row of 65,536
-//   scores is bound by its own request rate.
+//   positions (the score kernel counting each chunk's first digits, then
+//   chunk_thresh_kernel and chunk_final_kernel, below): a single workgroup
+//   reading a row of 65,536 scores is bound by its own request rate.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -56,11 +56,21 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kBins = 4096;       // radix histogram bins (12-bit digits)
 constexpr int kCandCap = 4096;    // keys sharing the first digit kept in LDS
 constexpr unsigned kNegInfKey = 0x007FFFFFu;  // order key of -inf
+// chunked selection (rows of more than kChunkedFrom positions)
+constexpr int kChunk = 4096;                       // positions per chunk
+constexpr int kChThreads = 256;                    // threads of a chunk workgroup
+constexpr int kChWaves = kChThreads / 64;
+constexpr int kChPer = kChunk / kChThreads;        // positions per thread
+constexpr int kCoarseBins = 256;                   // top 8 bits of a key
+constexpr int kHistU16 = kCoarseBins + kBins;      // per chunk: coarse counts, then first-digit counts
+constexpr int kChunkedFrom = 16 * kSelThreads;     // rows of up to this many positions: select_kernel
+constexpr int kHistWaves = 8;                      // waves of a score workgroup that also counts (HIST)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 // fp32 -> unsigned key with the same order (larger score, larger key; -0
 // and +0 are the same score).
@@ -73,21 +83,28 @@ __device__ __forceinline__ float key_score(unsigned k) {
     return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// grid (ceil(max_blocks / (kScoreWaves * kBlocksPerWave)), batch), 256 threads.
+// grid (ceil(max_blocks / (W * BPW)), batch), 64 W threads: W = kScoreWaves
+// waves of BPW = kBlocksPerWave blocks; with HIST (rows of more than
+// kChunkedFrom positions) W = kHistWaves waves of 8 blocks, so that a
+// workgroup scores one whole chunk of kChunk positions, and it also counts
+// the first digits of its candidates' keys per query row into the chunk
+// histograms of the chunked selection (hist, u16 [rows, nch, kHistU16]).
 // QL >= q_len query rows are held in registers: one row needs 76 VGPRs (six
 // waves per SIMD), four need 137 (three).
-template <int QL>
-__global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t* __restrict__ q_idx,
-                                                                  const uint8_t* __restrict__ k_cache,
-                                                                  int64_t num_kv_blocks,
-                                                                  const int32_t* __restrict__ block_table,
-                                                                  const int32_t* __restrict__ seq_lens, int q_len,
-                                                                  int max_blocks, float* __restrict__ scores) {
+template <int QL, bool HIST>
+__global__ __launch_bounds__(HIST ? 64 * kHistWaves : 64 * kScoreWaves) void score_kernel(
+    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ k_cache, int64_t num_kv_blocks,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int q_len, int max_blocks,
+    float* __restrict__ scores, uint16_t* __restrict__ hist) {
+    constexpr int W = HIST ? kHistWaves : kScoreWaves;
+    constexpr int BPW = HIST ? kChunk / (kBlk * kHistWaves) : kBlocksPerWave;
+    static_assert(!HIST || W * BPW * kBlk == kChunk, "a counting workgroup scores one chunk");
+    __shared__ unsigned hf[HIST ? QL * kBins : 1];
     // (sequence, chunk) items dealt XCD by XCD: consecutive workgroup ids go
     // round-robin over the 8 XCDs, XCD x takes the x-th eighth of the items, so
     // a sequence's scores land in the L2 of the XCD whose select workgroups read
     // them (the select kernel deals its rows the same way)
-    const int nchunk = (max_blocks + kScoreWaves * kBlocksPerWave - 1) / (kScoreWaves * kBlocksPerWave);
+    const int nchunk = (max_blocks + W * BPW - 1) / (W * BPW);
     const int nitems = (int)gridDim.x;
     const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
     const int item = xcd * (nitems >> 3) + min(xcd, nitems & 7) + within;
@@ -117,9 +134,13 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
         }
     }
 
+    if (HIST) {
+        for (int i = threadIdx.x; i < QL * kBins; i += 64 * W) hf[i] = 0;
+        __syncthreads();
+    }
 #pragma unroll 1
-    for (int i = 0; i < kBlocksPerWave; ++i) {
-        const int j = (chunk * kBlocksPerWave + i) * kScoreWaves + wave;  // logical block
+    for (int i = 0; i < BPW; ++i) {
+        const int j = (chunk * BPW + i) * W + wave;  // logical block
         if (j >= max_blocks || j * kBlk >= n) continue;
         const int blk = block_table[(int64_t)b * max_blocks + j];
         const int tok_end = min(kBlk, n - j * kBlk);
@@ -152,8 +173,36 @@ __global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(const uint16_t*
                 p += __shfl_xor(p, 8);
                 if (c == t) mine = p;   // token 4t + g
             }
-            if (mytok < tok_end) scores[(row0 + s) * cap + j * kBlk + mytok] = mine;
+            if (mytok < tok_end) {
+                scores[(row0 + s) * cap + j * kBlk + mytok] = mine;
+                if (HIST) {
+                    const unsigned key = order_key(mine);
+                    if (key > kNegInfKey) atomicAdd(&hf[s * kBins + (key >> 20)], 1u);
+                }
+            }
         }
+    }
+    if (HIST) {
+        // thread t < 256: first digits 16t .. 16t + 15 of each row, and their sum
+        // (the count of top-8-bit value t)
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < kCoarseBins)
+            for (int s = 0; s < q_len; ++s) {
+                uint16_t* h = hist + ((row0 + s) * nchunk + chunk) * kHistU16;
+                u16x8 lo, hi;
+                unsigned coarse = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned a = hf[s * kBins + 16 * t + e], bb = hf[s * kBins + 16 * t + 8 + e];
+                    lo[e] = (unsigned short)a;
+                    hi[e] = (unsigned short)bb;
+                    coarse += a + bb;
+                }
+                h[t] = (uint16_t)coarse;
+                *(u16x8*)(h + kCoarseBins + 16 * t) = lo;
+                *(u16x8*)(h + kCoarseBins + 16 * t + 8) = hi;
+            }
     }
 }
 
@@ -385,12 +434,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 // ---- chunked selection: rows of more than kChunkedFrom positions
 //
 // One workgroup of 256 threads per (row, chunk of kChunk positions), thread t
-// owning the 16 contiguous positions kChunk c + 16 t ..; three kernels, with
-// no atomics between workgroups (each kernel reads what the previous one
-// wrote):
-//   chunk_hist_kernel   the chunk's histogram of the first 12-bit digit of
-//                       its candidates' keys (u16 counts) and, from it, of
-//                       the top 8 bits (16 first digits each);
+// owning the 16 contiguous positions kChunk c + 16 t ..; with no atomics
+// between workgroups (each kernel reads what the previous one wrote):
+//   score_kernel<HIST>  (one workgroup per chunk) the chunk's histogram of the
+//                       first 12-bit digit of its candidates' keys (u16
+//                       counts) and, from it, of the top 8 bits (16 first
+//                       digits each), per query row;
 //   chunk_thresh_kernel every workgroup of a row sums the row's histograms:
 //                       the top 8 bits of the kk-th largest key from the
 //                       coarse counts, then its first digit T from the 16
@@ -404,15 +453,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 //                       entries of the earlier chunks above and equal to it,
 //                       and writes its chunk's winners at their slots.
 // The winners and their order are those of select_kernel.
-constexpr int kChunk = 4096;
-constexpr int kChThreads = 256;
-constexpr int kChWaves = kChThreads / 64;
-constexpr int kChPer = kChunk / kChThreads;        // positions per thread
-constexpr int kCoarseBins = 256;                   // top 8 bits of a key
-constexpr int kHistU16 = kCoarseBins + kBins;      // per chunk: coarse counts, then first-digit counts
-constexpr int kChunkedFrom = 16 * kSelThreads;     // rows of up to this many positions: select_kernel
 
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 // (row, chunk) of this workgroup: items r * nch_max + c dealt XCD by XCD, as
 // the score kernel deals a sequence's items, so a row's chunks and scores
@@ -459,41 +500,6 @@ __device__ __forceinline__ void sum_chunks(const uint16_t* h, int nch, int c, in
             before += c0 + j < c ? x : 0;
         }
     }
-}
-
-__global__ __launch_bounds__(kChThreads) void chunk_hist_kernel(const float* __restrict__ scores,
-                                                                const int32_t* __restrict__ seq_lens, int q_len,
-                                                                int max_blocks, int nch_max,
-                                                                uint16_t* __restrict__ hist) {
-    __shared__ unsigned hf[kBins];
-    int r, c;
-    chunk_item(nch_max, r, c);
-    const int64_t cap = (int64_t)kBlk * max_blocks;
-    const int n = row_positions(seq_lens, r, q_len, cap);
-    if (c * kChunk >= n) return;  // no such chunk: nothing reads its histogram
-    const int tid = threadIdx.x;
-    unsigned k[kChPer];
-    chunk_keys(scores + (int64_t)r * cap, c, n, k);
-    for (int i = tid; i < kBins; i += kChThreads) hf[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kChPer; ++j)
-        if (k[j] > kNegInfKey) atomicAdd(&hf[k[j] >> 20], 1u);
-    __syncthreads();
-    // thread t: first digits 16t .. 16t + 15, whose sum is the count of top-8-bit value t
-    uint16_t* h = hist + ((int64_t)r * nch_max + c) * kHistU16;
-    u16x8 lo, hi;
-    unsigned coarse = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const unsigned a = hf[16 * tid + e], b = hf[16 * tid + 8 + e];
-        lo[e] = (unsigned short)a;
-        hi[e] = (unsigned short)b;
-        coarse += a + b;
-    }
-    h[tid] = (uint16_t)coarse;
-    *(u16x8*)(h + kCoarseBins + 16 * tid) = lo;
-    *(u16x8*)(h + kCoarseBins + 16 * tid + 8) = hi;
 }
 
 __global__ __launch_bounds__(kChThreads) void chunk_thresh_kernel(const float* __restrict__ scores,
@@ -788,23 +794,25 @@ smla_status_t check_args(const void* q_idx, int32_t d_idx, const void* k_cache, 
     return SMLA_OK;
 }
 
+// hist != nullptr: the counting variant (one workgroup per chunk of kChunk positions)
 smla_status_t launch_scores(const void* q_idx, const void* k_cache, int64_t num_kv_blocks,
                             const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t q_len,
-                            int32_t max_blocks_per_seq, float* scores, hipStream_t st) {
-    const int per_wg = kScoreWaves * kBlocksPerWave;
+                            int32_t max_blocks_per_seq, float* scores, uint16_t* hist, hipStream_t st) {
+    const bool counting = hist != nullptr;
+    const int per_wg = counting ? kChunk / kBlk : kScoreWaves * kBlocksPerWave;
     dim3 g1((unsigned)((max_blocks_per_seq + per_wg - 1) / per_wg) * (unsigned)batch);
+    dim3 t1(counting ? 64 * kHistWaves : 64 * kScoreWaves);
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, g1, dim3(64 * kScoreWaves), 0, st, (const uint16_t*)q_idx,
-                           (const uint8_t*)k_cache, num_kv_blocks, block_table, seq_lens, (int)q_len,
-                           (int)max_blocks_per_seq, scores);
+        hipLaunchKernelGGL(kernel, g1, t1, 0, st, (const uint16_t*)q_idx, (const uint8_t*)k_cache, num_kv_blocks,
+                           block_table, seq_lens, (int)q_len, (int)max_blocks_per_seq, scores, hist);
     };
     static_assert(kMaxQlen == 4, "the score kernel is instantiated for up to four query rows");
     if (q_len == 1)
-        launch(score_kernel<1>);
+        counting ? launch(score_kernel<1, true>) : launch(score_kernel<1, false>);
     else if (q_len == 2)
-        launch(score_kernel<2>);
+        counting ? launch(score_kernel<2, true>) : launch(score_kernel<2, false>);
     else
-        launch(score_kernel<4>);
+        counting ? launch(score_kernel<4, true>) : launch(score_kernel<4, false>);
     return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -823,7 +831,7 @@ extern "C" smla_status_t smla_indexer_scores(const void* q_idx, int32_t d_idx, c
     if (!scores || ((uintptr_t)scores & 3)) return SMLA_ERR_INVALID_ARG;
     (void)hipGetLastError();
     return launch_scores(q_idx, k_cache, num_kv_blocks, block_table, seq_lens, batch, q_len, max_blocks_per_seq,
-                         scores, (hipStream_t)stream);
+                         scores, nullptr, (hipStream_t)stream);
 }
 
 extern "C" smla_status_t smla_indexer_topk(const void* q_idx, int32_t d_idx, const void* k_cache,
@@ -851,19 +859,18 @@ extern "C" smla_status_t smla_indexer_topk(const void* q_idx, int32_t d_idx, con
     (void)hipGetLastError();
     hipStream_t hs = (hipStream_t)stream;
     float* scores = (float*)workspace;
+    uint8_t* wb = (uint8_t*)workspace;
+    uint16_t* hist = cap > kChunkedFrom ? (uint16_t*)(wb + wl.hist) : nullptr;
     st = launch_scores(q_idx, k_cache, num_kv_blocks, block_table, seq_lens, batch, q_len, max_blocks_per_seq,
-                       scores, hs);
+                       scores, hist, hs);
     if (st != SMLA_OK) return st;
     if (cap > kChunkedFrom) {
-        // long rows: chunk histograms, threshold digit and candidate lists, then the winners
-        uint8_t* wb = (uint8_t*)workspace;
-        uint16_t* hist = (uint16_t*)(wb + wl.hist);
+        // long rows: the scores with their chunk histograms, then the threshold
+        // digit and candidate lists, then the winners
         int* cinfo = (int*)(wb + wl.cinfo);
         int* header = (int*)(wb + wl.header);
         unsigned* cand = (unsigned*)(wb + wl.cand);
         const dim3 g((unsigned)(rows * nch)), t(kChThreads);
-        hipLaunchKernelGGL(chunk_hist_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
-                           (int)nch, hist);
         hipLaunchKernelGGL(chunk_thresh_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
                            (int)nch, (int)topk, hist, cinfo, header, cand);
         hipLaunchKernelGGL(chunk_final_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
