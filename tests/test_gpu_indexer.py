@@ -183,6 +183,20 @@ def test_indexer_chunked_masks_and_short_rows():
     check(inp, 1000, idx, sc, ws, "chunked masks", block_table=bt, seq_lens=sl)
 
 
+@pytest.mark.parametrize("q_len", [3, 4])
+def test_indexer_chunked_multi_token_rows(q_len):
+    # three and four query rows per sequence on rows long enough for the chunked selection: the score
+    # kernel counts each row's chunk histograms separately (the four-row instantiation serves both);
+    # the second sequence's blocks are all out of range, so its rows have positions but no candidates
+    inp = I.small_indexer_inputs(batch=2, q_len=q_len, topk=500, seq_len=17500, seed=46 + q_len)
+    bt = inp.block_table.copy()
+    bt[1, :] = -1
+    note(f"indexer chunked q_len={q_len}")
+    idx, sc, ws = run_indexer(inp, 500, block_table=bt)
+    assert np.all(idx[1] == -1) and np.all(np.isneginf(sc[1]))
+    check(inp, 500, idx, sc, ws, f"chunked q_len={q_len}", block_table=bt)
+
+
 def test_indexer_rows_longer_than_registers():
     # more than 65536 positions per row: the selection streams the row from the workspace each pass
     inp = I.small_indexer_inputs(batch=2, q_len=1, topk=300, seq_len_range=(66000, 70000), seed=37)
