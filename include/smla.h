@@ -275,9 +275,9 @@ smla_status_t smla_combine(const void *part_out, const float *part_lse, int32_t 
  * 0 <= topk <= 2048 (else SMLA_ERR_UNSUPPORTED).  Pointer alignment: q_idx
  * and k_cache 16 bytes, the int32/fp32 arrays 4 bytes (else
  * SMLA_ERR_INVALID_ARG).  Kernels on `stream`: the scores, then the
- * selection (one kernel, or two when block_size * max_blocks_per_seq
- * exceeds 16,384); asynchronous; allocates nothing; the launch geometry
- * depends only on the sizes.
+ * selection (one kernel, or two or three when block_size *
+ * max_blocks_per_seq exceeds 16,384); asynchronous; allocates nothing; the
+ * launch geometry depends only on the sizes.
  */
 smla_status_t smla_indexer_workspace_size(int32_t batch, int32_t q_len, int32_t block_size,
                                           int32_t max_blocks_per_seq, uint64_t *bytes_out);

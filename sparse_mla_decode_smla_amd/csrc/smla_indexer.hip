@@ -33,9 +33,10 @@
 //                 (and the lowest positions of the threshold's ties) are
 //                 written in ascending position order with no sort.
 //   Longer rows take the same selection spread over one workgroup per 4096
-//   positions (the score kernel counting each chunk's first digits, then
-//   chunk_thresh_kernel and chunk_final_kernel, below): a single workgroup
-//   reading a row of 65,536 scores is bound by its own request rate.
+//   positions (each chunk's first digits counted by the score kernel or by
+//   chunk_hist_kernel, then chunk_thresh_kernel and chunk_final_kernel,
+//   below): a single workgroup reading a row of 65,536 scores is bound by its
+//   own request rate.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -65,6 +66,11 @@ constexpr int kCoarseBins = 256;                   // top 8 bits of a key
 constexpr int kHistU16 = kCoarseBins + kBins;      // per chunk: coarse counts, then first-digit counts
 constexpr int kChunkedFrom = 16 * kSelThreads;     // rows of up to this many positions: select_kernel
 constexpr int kHistWaves = 8;                      // waves of a score workgroup that also counts (HIST)
+// The score kernel counts the chunk histograms itself when it has at least
+// this many (sequence, chunk) workgroups, one per CU of an MI355X (with fewer
+// it streams the keys on too few CUs, and the histograms take a kernel of
+// their own)
+constexpr int kCountingFromWgs = 256;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -439,7 +445,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 //   score_kernel<HIST>  (one workgroup per chunk) the chunk's histogram of the
 //                       first 12-bit digit of its candidates' keys (u16
 //                       counts) and, from it, of the top 8 bits (16 first
-//                       digits each), per query row;
+//                       digits each), per query row; with fewer than
+//                       kCountingFromWgs (sequence, chunk) workgroups the
+//                       plain score kernel and chunk_hist_kernel instead;
 //   chunk_thresh_kernel every workgroup of a row sums the row's histograms:
 //                       the top 8 bits of the kk-th largest key from the
 //                       coarse counts, then its first digit T from the 16
@@ -500,6 +508,44 @@ __device__ __forceinline__ void sum_chunks(const uint16_t* h, int nch, int c, in
             before += c0 + j < c ? x : 0;
         }
     }
+}
+
+// The chunk histograms when the score kernel does not count them (fewer
+// (sequence, chunk) workgroups than kCountingFromWgs): one workgroup per
+// (row, chunk) reads the chunk's scores back.
+__global__ __launch_bounds__(kChThreads) void chunk_hist_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ seq_lens, int q_len,
+                                                                int max_blocks, int nch_max,
+                                                                uint16_t* __restrict__ hist) {
+    __shared__ unsigned hf[kBins];
+    int r, c;
+    chunk_item(nch_max, r, c);
+    const int64_t cap = (int64_t)kBlk * max_blocks;
+    const int n = row_positions(seq_lens, r, q_len, cap);
+    if (c * kChunk >= n) return;  // no such chunk: nothing reads its histogram
+    const int tid = threadIdx.x;
+    unsigned k[kChPer];
+    chunk_keys(scores + (int64_t)r * cap, c, n, k);
+    for (int i = tid; i < kBins; i += kChThreads) hf[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kChPer; ++j)
+        if (k[j] > kNegInfKey) atomicAdd(&hf[k[j] >> 20], 1u);
+    __syncthreads();
+    // thread t: first digits 16t .. 16t + 15, whose sum is the count of top-8-bit value t
+    uint16_t* h = hist + ((int64_t)r * nch_max + c) * kHistU16;
+    u16x8 lo, hi;
+    unsigned coarse = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const unsigned a = hf[16 * tid + e], b = hf[16 * tid + 8 + e];
+        lo[e] = (unsigned short)a;
+        hi[e] = (unsigned short)b;
+        coarse += a + b;
+    }
+    h[tid] = (uint16_t)coarse;
+    *(u16x8*)(h + kCoarseBins + 16 * tid) = lo;
+    *(u16x8*)(h + kCoarseBins + 16 * tid + 8) = hi;
 }
 
 __global__ __launch_bounds__(kChThreads) void chunk_thresh_kernel(const float* __restrict__ scores,
@@ -860,17 +906,23 @@ extern "C" smla_status_t smla_indexer_topk(const void* q_idx, int32_t d_idx, con
     hipStream_t hs = (hipStream_t)stream;
     float* scores = (float*)workspace;
     uint8_t* wb = (uint8_t*)workspace;
-    uint16_t* hist = cap > kChunkedFrom ? (uint16_t*)(wb + wl.hist) : nullptr;
+    const bool chunked = cap > kChunkedFrom;
+    const bool counting = chunked && (int64_t)batch * nch >= kCountingFromWgs;
+    uint16_t* hist = chunked ? (uint16_t*)(wb + wl.hist) : nullptr;
     st = launch_scores(q_idx, k_cache, num_kv_blocks, block_table, seq_lens, batch, q_len, max_blocks_per_seq,
-                       scores, hist, hs);
+                       scores, counting ? hist : nullptr, hs);
     if (st != SMLA_OK) return st;
-    if (cap > kChunkedFrom) {
-        // long rows: the scores with their chunk histograms, then the threshold
-        // digit and candidate lists, then the winners
+    if (chunked) {
+        // long rows: the chunk histograms (counted by the score kernel, or by a
+        // kernel of their own), then the threshold digit and candidate lists,
+        // then the winners
         int* cinfo = (int*)(wb + wl.cinfo);
         int* header = (int*)(wb + wl.header);
         unsigned* cand = (unsigned*)(wb + wl.cand);
         const dim3 g((unsigned)(rows * nch)), t(kChThreads);
+        if (!counting)
+            hipLaunchKernelGGL(chunk_hist_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len,
+                               (int)max_blocks_per_seq, (int)nch, hist);
         hipLaunchKernelGGL(chunk_thresh_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,
                            (int)nch, (int)topk, hist, cinfo, header, cand);
         hipLaunchKernelGGL(chunk_final_kernel, g, t, 0, hs, scores, seq_lens, (int)q_len, (int)max_blocks_per_seq,

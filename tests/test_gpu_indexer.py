@@ -151,12 +151,16 @@ def _periodic_keys(inp, period):
     return k2.reshape(inp.k_cache.shape)
 
 
-def test_indexer_chunked_ties_across_chunks():
+# Chunked selection: batches of a few sequences have the chunk histograms counted by a kernel of their
+# own; from 256 (sequence, chunk) workgroups on (here batch 52 or 64) the score kernel counts them.
+@pytest.mark.parametrize("batch", [3, 64])
+def test_indexer_chunked_ties_across_chunks(batch):
     # rows of 20480 (five whole chunks of 4096), 20481 (one position in a sixth) and 17000 positions,
     # each score value repeated every 7 positions: the threshold's ties spread over every chunk, and the
     # lowest positions among them must win, as in the oracle
-    inp = I.small_indexer_inputs(batch=3, q_len=1, topk=2048, seq_len=20481, seed=44)
-    sl = np.array([20480, 20481, 17000], dtype=np.int32)
+    inp = I.small_indexer_inputs(batch=batch, q_len=1, topk=2048, seq_len=20481, seed=44)
+    sl = np.full(batch, 20481, dtype=np.int32)
+    sl[[0, 2]] = [20480, 17000]
     inp2 = I.IndexerInputs(workload=inp.workload, q_idx=inp.q_idx, k_cache=_periodic_keys(inp, 7),
                            block_table=inp.block_table, seq_lens=sl)
     note(f"indexer chunked ties: seq_lens {sl.tolist()}")
@@ -166,10 +170,11 @@ def test_indexer_chunked_ties_across_chunks():
     assert np.array_equal(idx, ref), "with exact ties the selection must be the oracle's"
 
 
-def test_indexer_chunked_masks_and_short_rows():
+@pytest.mark.parametrize("batch", [4, 52])
+def test_indexer_chunked_masks_and_short_rows(batch):
     # rows long enough for the chunked selection: an empty row, a row with fewer candidates than the list
     # (its last chunk one position long), bad block ids inside chunks
-    inp = I.small_indexer_inputs(batch=4, q_len=2, topk=1000, seq_len=18000, seed=45)
+    inp = I.small_indexer_inputs(batch=batch, q_len=2, topk=1000, seq_len=18000, seed=45)
     bt = inp.block_table.copy()
     sl = inp.seq_lens.copy()
     sl[0] = 0                                    # no candidates
@@ -183,12 +188,12 @@ def test_indexer_chunked_masks_and_short_rows():
     check(inp, 1000, idx, sc, ws, "chunked masks", block_table=bt, seq_lens=sl)
 
 
-@pytest.mark.parametrize("q_len", [3, 4])
-def test_indexer_chunked_multi_token_rows(q_len):
-    # three and four query rows per sequence on rows long enough for the chunked selection: the score
-    # kernel counts each row's chunk histograms separately (the four-row instantiation serves both);
+@pytest.mark.parametrize("q_len,batch", [(3, 2), (4, 2), (3, 52)])
+def test_indexer_chunked_multi_token_rows(q_len, batch):
+    # three and four query rows per sequence on rows long enough for the chunked selection (at batch 52
+    # the score kernel counts each row's chunk histograms, its four-row instantiation serving three);
     # the second sequence's blocks are all out of range, so its rows have positions but no candidates
-    inp = I.small_indexer_inputs(batch=2, q_len=q_len, topk=500, seq_len=17500, seed=46 + q_len)
+    inp = I.small_indexer_inputs(batch=batch, q_len=q_len, topk=500, seq_len=17500, seed=46 + q_len)
     bt = inp.block_table.copy()
     bt[1, :] = -1
     note(f"indexer chunked q_len={q_len}")
