@@ -120,6 +120,20 @@ def test_masking_edge_cases(fmt, topk, seq_len):
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
+def test_unaligned_lists_and_table_rows(fmt):
+    # top-k 702 and 259-entry block-table rows: the index list of row 1 and the table rows of sequences
+    # 1 and 2 start 8, 12 and 8 bytes past a 16-byte boundary, so their whole 256-entry chunks are copied
+    # entry by entry, while the others take the 16-byte copies; parts of 702 and of 352 entries
+    inp = I.small_inputs(batch=3, q_len=1, topk=702, seq_len=259 * 64 - 10, kv_format=fmt, seed=70 + fmt)
+    assert inp.block_table.shape[1] == 259
+    note(f"unaligned lists and table rows fmt={fmt}")
+    ref_o, ref_l = oracle.decode_inputs(inp, threads=8)
+    for splits in (1, 2):
+        out, lse = run_gpu(inp, force_splits=splits)
+        check(out, lse, ref_o, ref_l, f"unaligned fmt{fmt} S{splits}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
 def test_seq_lens_optional(fmt):
     inp = I.small_inputs(batch=2, q_len=1, topk=96, seq_len=256, kv_format=fmt, seed=31)
     sl = np.array([256, 120], dtype=np.int32)
