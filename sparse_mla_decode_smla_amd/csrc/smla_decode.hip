@@ -382,35 +382,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     g_u16* const obase = (g_u16*)(uintptr_t)(a.num_splits == 1 ? out_p : part_p) + orow * kHeads * kDv;
     g_f32* const lbase = (g_f32*)(uintptr_t)(a.num_splits == 1 ? lse_p : plse_p) + orow * kHeads;
     auto store_all = [&]() {
-        // wave w stores heads 8w .. 8w + 7; lane l holds dims [4l, 4l + 4) and
-        // [256 + 4l, 256 + 4l + 4); all sixteen LDS reads first
-        i32x2 xs[8][2];
+        // wave w stores heads 8w .. 8w + 7; lane l holds dims [8l, 8l + 8); all
+        // eight LDS reads first
+        i32x4 xs[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int h = 8 * wave + j;
-            xs[j][0] = lds_load<i32x2>(lds + h * kRowPitch + 8 * lane);
-            xs[j][1] = lds_load<i32x2>(lds + h * kRowPitch + 512 + 8 * lane);
-        }
+        for (int j = 0; j < 8; ++j) xs[j] = lds_load<i32x4>(lds + (8 * wave + j) * kRowPitch + 16 * lane);
         __builtin_amdgcn_sched_barrier(0);
         // (several parts: bf16 partials, rounded once more than the output; the
         // combine adds them in fp32)
-        typedef __attribute__((address_space(1))) i32x2 g_i32x2;
+        typedef __attribute__((address_space(1))) i32x4 g_i32x4;
         if (a.stream_out) {
             // (non-temporal stores written out: with the builtin, the compiler merged
             // the two branches' identical stores and dropped the hint)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
-                asm volatile("global_store_dwordx2 %0, %1, off nt\n\tglobal_store_dwordx2 %0, %2, off offset:512 nt"
-                             ::"v"(o), "v"(xs[j][0]), "v"(xs[j][1])
-                             : "memory");
+                g_u16* o = obase + (8 * wave + j) * kDv + 8 * lane;
+                asm volatile("global_store_dwordx4 %0, %1, off nt" ::"v"(o), "v"(xs[j]) : "memory");
             }
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                g_u16* o = obase + (8 * wave + j) * kDv + 4 * lane;
-                *(g_i32x2*)o = xs[j][0];
-                *(g_i32x2*)(o + 256) = xs[j][1];
+                g_u16* o = obase + (8 * wave + j) * kDv + 8 * lane;
+                *(g_i32x4*)o = xs[j];
             }
         }
     };
