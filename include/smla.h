@@ -90,9 +90,9 @@ typedef enum {
  * arithmetic, and so every result, is the same under every policy.
  * SMLA_CACHE_AUTO lets the plan choose from the problem shape: streaming rows
  * when the call writes at least 4 MiB of results or may gather at least 64 MiB;
- * streaming outputs too when it writes at least 4 MiB and either has one part
- * or gathers at least 64 MiB (otherwise the combine kernel reads the parts from
- * the cache); else cached (thresholds set by measurement on MI355X). */
+ * streaming the output too when it writes at least 4 MiB with one part (with
+ * several parts the combine kernel reads them from the cache); else cached
+ * (thresholds set by measurement on MI355X). */
 typedef enum {
     SMLA_CACHE_AUTO = 0,
     SMLA_CACHE_CACHED = 1,          /* rows and outputs through the caches as ordinary accesses */

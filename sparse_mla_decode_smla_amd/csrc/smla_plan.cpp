@@ -83,10 +83,10 @@ int choose_cache_policy(const smla_problem_t& p, int rows, int splits) {
     const double gathered = (double)rows * p.topk * smla::gathered_bytes_per_token(p.kv_format);
     const double written = (double)rows * splits * smla::kHeads * smla::kDv * 2.0;
     const bool big_out = written >= 4.0 * (1 << 20), big_rows = gathered >= 64.0 * (1 << 20);
-    // results streamed too when nothing reads them back (one part) or when the
-    // row stream is large; several parts otherwise stay cached for the combine
-    // kernel, which reads them from the L2 of the XCD that wrote them
-    if (big_out && (splits == 1 || big_rows)) return SMLA_CACHE_STREAM_BOTH;
+    // results streamed too when nothing reads them back (one part); several
+    // parts stay cached for the combine kernel, which reads them from the L2
+    // of the XCD that wrote them
+    if (big_out && splits == 1) return SMLA_CACHE_STREAM_BOTH;
     return big_out || big_rows ? SMLA_CACHE_STREAM_ROWS : SMLA_CACHE_CACHED;
 }
 

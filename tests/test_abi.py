@@ -69,7 +69,7 @@ PLANNED_SPLITS = {"b1_topk512_n4096_contiguous_bf16": 16, "b1_topk2048_n32768_pa
 # bytes), else cached
 PLANNED_POLICY = {"b1_topk512_n4096_contiguous_bf16": B.CACHE_CACHED, "b1_topk2048_n32768_paged_bf16": B.CACHE_CACHED,
                   "b16_topk2048_n65536_paged_bf16": B.CACHE_STREAM_ROWS,
-                  "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_BOTH,
+                  "b64_topk2048_n1k-128k_paged_bf16": B.CACHE_STREAM_ROWS,
                   "b128_q2_topk2048_n65536_paged_fp8": B.CACHE_STREAM_BOTH,
                   "b1_topk512_n8192_paged_v4fp8": B.CACHE_CACHED, "b64_topk512_n8192_paged_v4fp8": B.CACHE_STREAM_ROWS}
 
@@ -103,8 +103,8 @@ def test_plan_cache_policy_thresholds():
     assert parts_below.cache_policy == B.CACHE_CACHED
     many = B.decode_plan(29, 1, 2048, 64, num_cus=256, force_splits=2)     # 65.3 MiB rows, 3.6 MiB of parts
     assert many.cache_policy == B.CACHE_STREAM_ROWS
-    both = B.decode_plan(64, 1, 2048, 64, num_cus=256, force_splits=2)     # 144 MiB rows, 8 MiB of parts
-    assert both.cache_policy == B.CACHE_STREAM_BOTH
+    big = B.decode_plan(64, 1, 2048, 64, num_cus=256, force_splits=2)      # 144 MiB rows, 8 MiB of parts
+    assert big.cache_policy == B.CACHE_STREAM_ROWS                         # parts cached whatever the rows
     for bad in (-1, 5):
         with pytest.raises(B.SmlaError):
             B.decode_plan(1, 1, 64, 4, num_cus=256, cache_policy=bad)
