@@ -202,6 +202,17 @@ def test_indexer_chunked_multi_token_rows(q_len, batch):
     check(inp, 500, idx, sc, ws, f"chunked q_len={q_len}", block_table=bt)
 
 
+@pytest.mark.parametrize("topk", [1, 63])
+@pytest.mark.parametrize("batch", [2, 52])
+def test_indexer_chunked_short_lists(topk, batch):
+    # the chunked selection with lists far shorter than a chunk's candidates: top-1 (the row's maximum,
+    # wherever it lies) and 63, with the histograms counted by their own kernel (batch 2) and by the
+    # score kernel (batch 52)
+    inp = I.small_indexer_inputs(batch=batch, q_len=1, topk=topk, seq_len=17000, seed=48 + topk)
+    idx, sc, ws = run_indexer(inp, topk)
+    check(inp, topk, idx, sc, ws, f"chunked top-{topk} batch {batch}")
+
+
 def test_indexer_rows_longer_than_registers():
     # more than 65536 positions per row: the selection streams the row from the workspace each pass
     inp = I.small_indexer_inputs(batch=2, q_len=1, topk=300, seq_len_range=(66000, 70000), seed=37)
